@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of DCA prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu]
+
+A step is one pass of the whole path over one batch of synthetic input:
+the remap pre-pass (cos/sin table + rotated query variants, rotated keys and
+value re-layout), the vertical-slash tile index for sparse workloads, and the
+attention kernel -- the same launches dca_prefill makes, issued through its
+stage entry points so that HIP events on the launch stream time each kernel.
+
+Prints ONE JSON line. `value` is whole-step TFLOP/s on the 1M-token Qwen2.5-14B
+layer shape (dense causal work 4 d Hq S(S+1)/2); `roofline` reports the
+attention kernel against the bf16 dense MFMA peak; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload; `extra` holds the other
+measured workloads (128K dense and 1M vertical-slash).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from position_extrapolation_amd import api, synth, workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def remap_bytes(w) -> float:
+    """Algorithmic bytes of the pre-pass: read q, k, v once; write three
+    rotated query variants, the rotated keys and the value re-layout; plus
+    the float32 cos/sin table for positions [0, C + W)."""
+    e = 2 if w.dtype == "bf16" else 4
+    per_tok = (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim * e           # read
+    per_tok += (3 * w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim * e      # write
+    table = (w.chunk + w.window) * (w.head_dim // 2) * 8
+    return float(per_tok * w.seq * w.batch + table)
+
+
+def vs_active_pairs(w, vert, slash) -> float:
+    """Causal (query, key) pairs inside active 64x64 tiles, summed over heads:
+    the attention work of a vertical-slash workload (pairs x 4 d flops).
+
+    Per query tile t the active key tiles are A = {kt in VT, kt <= t} united
+    with B = {t - delta : delta in D, delta <= t}; |A u B| = |A| + |B| - |A n B|
+    and |A n B| = sum_delta 1_D(delta) 1_VT(t - delta) is a convolution."""
+    from scipy.signal import fftconvolve
+
+    S = w.seq
+    n = (S + 63) // 64
+    t = np.arange(n)
+    rows_in = np.minimum(S - 64 * t, 64).astype(np.float64)   # valid rows of query tile t
+    total = 0.0
+    for h in range(w.n_q_heads):
+        ind_v = np.zeros(n)
+        ind_v[np.unique(np.asarray(vert[h], dtype=np.int64) // 64)] = 1
+        sl = np.asarray(slash[h], dtype=np.int64)
+        a = sl // 64
+        dset = np.unique(np.concatenate([a, (a + 1)[sl % 64 != 0]]))
+        ind_d = np.zeros(n)
+        ind_d[dset[dset < n]] = 1
+        n_a = np.cumsum(ind_v)                                  # |A|
+        n_b = np.cumsum(ind_d)                                  # |B|
+        n_ab = np.rint(fftconvolve(ind_d, ind_v)[:n])           # |A n B|
+        count = n_a + n_b - n_ab
+        diag = np.maximum(ind_v, ind_d[0])                      # tile (t, t) active
+        total += float((rows_in * 64 * (count - diag) + diag * rows_in * (rows_in + 1) / 2).sum())
+    return total * w.batch
+
+
+class Runner:
+    """Holds device inputs and workspace for one workload; runs one step."""
+
+    def __init__(self, w, device, seed=0):
+        self.w = w
+        log(f"[bench] generating inputs for {w.name}")
+        self.q, self.k, self.v = synth.make_qkv(w, seed=seed, device=device)
+        self.shape = api.shape_of(self.q, self.k)
+        self.vert = self.slash = None
+        self.mask = None
+        if w.sparse:
+            vn, sn = synth.vs_mask(w.n_q_heads, w.seq, w.n_vertical, w.n_slash, seed=seed)
+            self.vert_host, self.slash_host = vn, sn
+            self.vert = torch.from_numpy(vn).to(device)
+            self.slash = torch.from_numpy(sn).to(device)
+            self.mask = api.make_mask(self.vert, self.slash)
+        self.nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, self.shape, self.mask)
+        self.ws = api.alloc_workspace(self.nbytes, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=device)
+        self.ev = None
+
+    def step(self, events=None):
+        w = self.w
+        if events is not None:
+            events[0].record()
+        api.dca_remap(self.q, self.k, self.v, w.seq, w.chunk, w.window, w.rope_base, self.shape, self.ws,
+                      self.nbytes)
+        if events is not None:
+            events[1].record()
+        if self.mask is not None:
+            api.dca_vs_index(w.seq, w.chunk, w.window, self.mask, self.shape, self.ws, self.nbytes)
+        if events is not None:
+            events[2].record()
+        api.dca_attention(self.out, self.lse, w.seq, w.chunk, w.window, w.yarn_scale, self.mask, self.shape,
+                          self.ws, self.nbytes)
+        if events is not None:
+            events[3].record()
+
+    def time(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+            log(f"[bench] {self.w.name}: step {i + 1}/{steps} enqueued")
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        remap_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        index_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+        return wall * 1e3 / steps, remap_ms, index_ms, attn_ms
+
+    def work_flops(self):
+        w = self.w
+        if not w.sparse:
+            return w.dense_flops()
+        return 4.0 * w.head_dim * vs_active_pairs(w, self.vert_host, self.slash_host)
+
+
+def measure(name, steps, warmup, device):
+    w = workloads.get(name)
+    r = Runner(w, device)
+    ms, remap_ms, index_ms, attn_ms = r.time(steps, warmup)
+    flops = r.work_flops()
+    res = {
+        "workload": name, "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+        "attention_ms": attn_ms, "attention_tflops": flops / (attn_ms * 1e-3) / 1e12,
+        "remap_ms": remap_ms, "remap_gbs": remap_bytes(w) / (remap_ms * 1e-3) / 1e9,
+        "flops": flops,
+    }
+    if w.sparse:
+        res["vs_index_ms"] = index_ms
+        res["dense_equiv_tflops"] = w.dense_flops() / (ms * 1e-3) / 1e12
+        res["active_fraction"] = flops / w.dense_flops()
+    log(f"[bench] {name}: {json.dumps(res)}")
+    del r
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def cpu_baseline(name, n_rows=8, seed=0):
+    """The CPU oracle, as it stands, on a bounded sample of the workload:
+    n_rows query rows spread over the sequence, every head. Reported in the
+    benchmark's unit (TFLOP/s of the sampled rows' causal work)."""
+    from oracle import dca_oracle as O
+
+    w = workloads.get(name)
+    q, k, v = synth.make_qkv(w, seed=seed, device="cuda:0")
+    rows = torch.linspace(0, w.seq - 1, n_rows).round().long()
+    q_rows = q[:, :, rows.to(q.device)].cpu()
+    kc, vc = k.cpu(), v.cpu()
+    del q, k, v
+    torch.cuda.empty_cache()
+    threads = torch.get_num_threads()
+    t0 = time.perf_counter()
+    O.dca_prefill_rows(q_rows, rows, kc, vc, w.chunk, w.window, w.rope_base, w.yarn_scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * w.n_q_heads * w.batch * float((rows + 1).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} query rows evenly spread over {w.name} (S={w.seq}), all {w.n_q_heads} "
+                      f"heads, float64 torch-CPU oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="qwen14b_1m")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 128K and vertical-slash workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path is single-GPU (multi-GPU sharding is a design "
+              "note, not implemented); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    api.lib()
+    dev = "cuda:0"
+
+    w, main_res = measure(args.workload, args.steps, args.warmup, dev)
+    extra = []
+    if not args.no_extra:
+        for name in ("qwen7b_128k", "qwen14b_1m_vs"):
+            if name != args.workload:
+                steps = 10 if name == "qwen7b_128k" else max(1, args.steps)
+                extra.append(measure(name, steps, 2 if name == "qwen7b_128k" else 1, dev)[1])
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = main_res["attention_tflops"]
+    result = {
+        "metric": "DCA prefill attention TFLOP/s (1M tokens, Qwen2.5-14B layer shape, one MI355X)",
+        "value": round(main_res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1)*0.5 bf16 q/k/v)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "seq_len": w.seq,
+                   "chunk": w.chunk, "window": w.window, "rope_base": w.rope_base,
+                   "yarn_scale": round(w.yarn_scale, 10), "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * main_res["tflops"] / peak, 2),
+        "roofline": {"kernel": "dca_attention_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+        "remap": {"kernel": "remap_kernel", "bound": "hbm", "ms": round(main_res["remap_ms"], 3),
+                  "achieved": round(main_res["remap_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(main_res["remap_gbs"] / PEAK_HBM_GBS, 4)},
+        "attention_ms": round(main_res["attention_ms"], 3),
+        "extra": extra,
+    }
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w.name, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * dca.h -- C ABI of libdca: causal GQA prefill attention under Dual Chunk
+ * Attention (DCA) on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages):
+ *   [mizuki] "Qwen2.5-1M 不重训外推 1M", mizuki-eaf.pages.dev: sections
+ *            "核心思想" (the L x L attention matrix split into intra-chunk,
+ *            successive-chunk and inter-chunk parts), "Intra-Chunk Attention",
+ *            "Successive-Chunk Attention" (local window W), "Inter-Chunk
+ *            Attention" (query pinned at a large fixed index, key positions
+ *            repeating periodically), "DCA + YaRN" (temperature on the
+ *            logits), and the MInference vertical-slash sections.
+ *   [yudong] "Qwen-2.5 explained", yudonglee.me, section 3: GQA at every
+ *            size, RoPE base 1e7.
+ *
+ * What the library computes, for query head h, batch b, row i and every key
+ * j <= i (and only keys in active tiles when a vertical-slash mask is given):
+ *
+ *   c(i) = i / C, r(i) = i mod C, P = C + W - 1 (pinned query index)
+ *   key position        Pk(j)       = j mod C
+ *   intra  (c(i)=c(j))  Pq(i)       = r(i)
+ *   succ   (c(i)=c(j)+1) Pq(i)      = min(C + r(i), P)
+ *   inter  (otherwise)  Pq(i)       = P
+ *   s_ij  = yarn_scale * softmax_scale * < R(Pq(i)) q_i , R(Pk(j)) k_j >
+ *   out_i = sum_j softmax_j(s_i.) v_j          lse_i = ln sum_j exp(s_ij)
+ *
+ * R(p) is half-split RoPE: pairs (m, m + d/2) rotated by p * base^(-2m/d);
+ * cos and sin are taken in float64 and rounded to float32. KV head of query
+ * head h is h / (n_q_heads / n_kv_heads).
+ *
+ * Conventions for every entry point:
+ *   - Return value: a dca_status. On DCA_E_INVALID, DCA_E_UNSUPPORTED or
+ *     DCA_E_WORKSPACE nothing is enqueued and no output is touched; the
+ *     reason is in dca_last_error() (thread-local, valid until the next call
+ *     on the same thread). Nothing is thrown or aborted across the ABI.
+ *   - Device entry points enqueue on `stream` (a hipStream_t; NULL = the
+ *     null stream) and return without synchronizing. Results are valid
+ *     after the stream is synchronized. Launch failures return DCA_E_DEVICE.
+ *   - Pointers marked "device" are caller-owned device memory; the library
+ *     allocates and frees nothing.
+ *   - Tensors are contiguous row-major; q, out: [batch, n_q_heads, seq,
+ *     head_dim]; k, v: [batch, n_kv_heads, seq, head_dim]; all four share one
+ *     dtype. lse: [batch, n_q_heads, seq] float32.
+ *   - q, k, v and out must be 16-byte aligned, lse and mask lists 4-byte.
+ *   - Supported domain: head_dim 64 or 128; n_q_heads % n_kv_heads == 0;
+ *     seq >= 1 (ragged tails are handled); C >= 64 and C % 64 == 0;
+ *     0 <= W <= C; rope_base > 1; yarn_scale > 0; seq and C + W below 2^31.
+ *   - Calls are deterministic (bit-identical results for identical inputs)
+ *     and re-entrant; calls that share a workspace must not overlap.
+ */
+#ifndef DCA_H
+#define DCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DCA_OK = 0,
+    DCA_E_INVALID = 1,      /* a null pointer, a bad size, aliasing outputs */
+    DCA_E_UNSUPPORTED = 2,  /* valid but outside the supported domain */
+    DCA_E_WORKSPACE = 3,    /* workspace smaller than dca_workspace_size */
+    DCA_E_DEVICE = 4        /* HIP runtime or launch failure, or no GPU */
+} dca_status;
+
+typedef enum { DCA_F32 = 0, DCA_BF16 = 1 } dca_dtype;
+
+typedef struct {
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;          /* dca_dtype */
+    float softmax_scale;    /* 0 => 1 / sqrt(head_dim) */
+} dca_shape;
+
+/* MInference-style vertical-slash mask [mizuki, sparse-attention sections],
+ * read tile-granular on 64 x 64 (query, key) tiles: tile (t, kt), kt <= t, is
+ * active for query head h iff some vertical column of h lies in
+ * [64 kt, 64 kt + 63] or some slash offset of h lies in
+ * [max(0, 64 (t - kt) - 63), 64 (t - kt) + 63]. Columns and offsets are true
+ * indices (key j, distance i - j), not remapped positions. Every causal pair
+ * inside an active tile is attended; none in an inactive tile. The same mask
+ * applies to every batch entry. Entries outside [0, seq) are ignored; order
+ * and duplicates do not matter. */
+typedef struct {
+    const int32_t *vertical;  /* device [n_q_heads][n_vertical] */
+    const int32_t *slash;     /* device [n_q_heads][n_slash]    */
+    int32_t n_vertical;       /* >= 0 */
+    int32_t n_slash;          /* >= 0 */
+} dca_vs_mask;
+
+/* Text for a status code (static storage). */
+const char *dca_status_str(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char *dca_last_error(void);
+
+/* Host-only position-index map [mizuki, Intra-/Successive-/Inter-Chunk]:
+ * pq_intra[i] = i mod C, pq_succ[i] = min(C + i mod C, C + W - 1),
+ * *pq_inter = C + W - 1, pk[j] = j mod C, for i, j in [0, seq). Host arrays
+ * of seq int32 each (pq_inter: one int32), caller-owned; any of them may be
+ * NULL to skip it. */
+int dca_remap_positions(int64_t seq, int64_t C, int64_t W,
+                        int32_t *pq_intra, int32_t *pq_succ, int32_t *pq_inter,
+                        int32_t *pk);
+
+/* Bytes of device workspace dca_prefill needs for these arguments (mask may
+ * be NULL for dense causal). Written to *bytes. The workspace holds the
+ * float32 cos/sin table for positions [0, C + W), the three rotated query
+ * variants, the rotated keys and the re-laid-out values in the attention
+ * kernel's operand order, and (with a mask) the per-head tile lists. */
+int dca_workspace_size(int64_t seq, int64_t C, int64_t W, const dca_shape *shape,
+                       const dca_vs_mask *mask, size_t *bytes);
+
+/* The whole path [mizuki, 核心思想 through DCA + YaRN]: remap pre-pass
+ * (cos/sin table, rotated Q variants, rotated K, value re-layout), the
+ * vertical-slash tile index when mask != NULL, and the
+ * attention kernel. q, k, v: device, read-only. out: device, written for
+ * every (b, h, i < seq, d). lse: device float32 or NULL (skip). workspace:
+ * device, at least dca_workspace_size bytes, 256-byte aligned. out and lse
+ * must not overlap q, k, v or the workspace (DCA_E_INVALID). */
+int dca_prefill(const void *q, const void *k, const void *v, void *out, float *lse,
+                int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale,
+                const dca_vs_mask *mask, const dca_shape *shape,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* The three stages of dca_prefill, callable one at a time on the same
+ * workspace (for per-stage timing and checks):
+ *   dca_remap      -- the RoPE/DCA pre-pass: writes the cos/sin table, the
+ *                     three rotated query variants, the rotated keys and the
+ *                     value re-layout into the workspace [mizuki, Inter-Chunk:
+ *                     only position indices change].
+ *   dca_vs_index   -- mask -> per-head sorted key-tile list VT_h (tiles
+ *                     holding a vertical column) and tile-distance list D_h
+ *                     (distances delta < ceil(seq/64) whose slash interval
+ *                     [max(0, 64 delta - 63), 64 delta + 63] holds an offset);
+ *                     tile (t, kt) is active iff kt in VT_h or t - kt in D_h.
+ *   dca_attention  -- the flash-style kernel over the workspace written by
+ *                     dca_remap (and dca_vs_index when mask != NULL).
+ * Arguments have the meaning they have in dca_prefill; each stage validates
+ * them the same way. dca_attention needs the same seq, C, W, shape and mask
+ * as the dca_remap / dca_vs_index calls that filled the workspace. */
+int dca_remap(const void *q, const void *k, const void *v,
+              int64_t seq, int64_t C, int64_t W, double rope_base,
+              const dca_shape *shape, void *workspace, size_t workspace_bytes,
+              void *stream);
+int dca_vs_index(int64_t seq, int64_t C, int64_t W, const dca_vs_mask *mask,
+                 const dca_shape *shape, void *workspace, size_t workspace_bytes,
+                 void *stream);
+int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W,
+                  float yarn_scale, const dca_vs_mask *mask, const dca_shape *shape,
+                  const void *workspace, size_t workspace_bytes, void *stream);
+
+/* Checks (device): read back what the GPU stages computed.
+ *
+ * dca_debug_positions -- the device's own position map (the integer code the
+ *   pre-pass runs) into device int32 arrays of seq entries each:
+ *   pq_intra, pq_succ, pk; *pq_inter (device, one int32). All non-NULL.
+ * dca_debug_tile_regions -- the device's classification of every 64 x 64
+ *   (query tile, key tile) pair: out[t * n + kt] (device uint8, n =
+ *   ceil(seq/64), n * n entries) = 0 intra, 1 successive, 2 inter, 255 for
+ *   kt > t (not causal).
+ * dca_debug_unpack -- copy one pre-pass array out of a workspace filled by
+ *   dca_remap, in plain row-major [batch, heads, seq, head_dim] order and the
+ *   shape's dtype: which = 0 Q intra, 1 Q successive, 2 Q inter (n_q_heads),
+ *   3 rotated K, 4 V (n_kv_heads). dst: device.
+ * dca_debug_vs_lists -- copy the tile lists dca_vs_index wrote: vt and dl
+ *   are device int32 [n_q_heads][n_tiles] (n_tiles = ceil(seq/64)), counts
+ *   device int32 [n_q_heads] each. */
+int dca_debug_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra,
+                        int32_t *pq_succ, int32_t *pq_inter, int32_t *pk, void *stream);
+int dca_debug_tile_regions(int64_t seq, int64_t C, uint8_t *out, void *stream);
+int dca_debug_unpack(const void *workspace, size_t workspace_bytes, int which,
+                     int64_t seq, int64_t C, int64_t W, const dca_shape *shape,
+                     void *dst, void *stream);
+int dca_debug_vs_lists(const void *workspace, size_t workspace_bytes, int64_t seq,
+                       int64_t C, int64_t W, const dca_vs_mask *mask, const dca_shape *shape,
+                       int32_t *vt, int32_t *vt_count, int32_t *dl, int32_t *dl_count,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCA_H */

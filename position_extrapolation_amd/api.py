@@ -1,0 +1,234 @@
+"""Thin Python binding of libdca (include/dca.h): argument marshalling only.
+
+Every function named dca_* calls the C entry point of the same name through
+ctypes; torch is used for device memory and the current HIP stream. The
+library must be built (python -m position_extrapolation_amd.build); there is
+no fallback path -- a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdca.so")
+
+DCA_OK, DCA_E_INVALID, DCA_E_UNSUPPORTED, DCA_E_WORKSPACE, DCA_E_DEVICE = range(5)
+DCA_F32, DCA_BF16 = 0, 1
+
+EXPORTS = [
+    "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
+    "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
+    "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
+]
+
+
+class DcaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class dca_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class dca_vs_mask(ctypes.Structure):
+    _fields_ = [("vertical", ctypes.c_void_p), ("slash", ctypes.c_void_p),
+                ("n_vertical", ctypes.c_int32), ("n_slash", ctypes.c_int32)]
+
+
+_lib = None
+
+_I64, _I32P, _VP = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+_SIGS = {
+    "dca_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "dca_last_error": (ctypes.c_char_p, []),
+    "dca_remap_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP]),
+    "dca_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
+    "dca_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double,
+                                   ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_remap": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double, _VP, _VP,
+                                 ctypes.c_size_t, _VP]),
+    "dca_vs_index": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, ctypes.c_float, _VP, _VP, _VP,
+                                     ctypes.c_size_t, _VP]),
+    "dca_debug_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "dca_debug_tile_regions": (ctypes.c_int, [_I64, _I64, _VP, _VP]),
+    "dca_debug_unpack": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _I64, _I64, _I64, _VP, _VP, _VP]),
+    "dca_debug_vs_lists": (ctypes.c_int, [_VP, ctypes.c_size_t, _I64, _I64, _I64, _VP, _VP, _VP, _VP,
+                                          _VP, _VP, _VP]),
+}
+
+
+def lib():
+    """Load libdca.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m position_extrapolation_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def dca_status_str(status: int) -> str:
+    return lib().dca_status_str(status).decode()
+
+
+def dca_last_error() -> str:
+    return lib().dca_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != DCA_OK:
+        raise DcaError(status, where, f"{dca_status_str(status)}: {dca_last_error()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, dtype, softmax_scale=0.0) -> dca_shape:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}[dtype]
+    return dca_shape(batch, n_q_heads, n_kv_heads, head_dim, dtype, softmax_scale)
+
+
+def shape_of(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0) -> dca_shape:
+    return make_shape(q.shape[0], q.shape[1], k.shape[1], q.shape[3], q.dtype, softmax_scale)
+
+
+def make_mask(vertical: torch.Tensor | None, slash: torch.Tensor | None) -> dca_vs_mask | None:
+    """vertical [Hq, nv], slash [Hq, ns]: device int32 tensors (kept alive by the caller)."""
+    if vertical is None and slash is None:
+        return None
+    nv = 0 if vertical is None else vertical.shape[1]
+    ns = 0 if slash is None else slash.shape[1]
+    return dca_vs_mask(_ptr(vertical), _ptr(slash), nv, ns)
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+# ---- entry points, same names as include/dca.h ---------------------------
+
+def dca_remap_positions(seq: int, C: int, W: int):
+    """Host position map -> (pq_intra, pq_succ, pq_inter, pk) as int32 tensors."""
+    pqi = torch.empty(seq, dtype=torch.int32)
+    pqs = torch.empty(seq, dtype=torch.int32)
+    pk = torch.empty(seq, dtype=torch.int32)
+    pinter = torch.empty(1, dtype=torch.int32)
+    _check(lib().dca_remap_positions(seq, C, W, _ptr(pqi), _ptr(pqs), _ptr(pinter), _ptr(pk)),
+           "dca_remap_positions")
+    return pqi, pqs, int(pinter[0]), pk
+
+
+def dca_workspace_size(seq: int, C: int, W: int, shape: dca_shape, mask: dca_vs_mask | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dca_workspace_size(seq, C, W, ctypes.byref(shape), _ref(mask), ctypes.byref(n)),
+           "dca_workspace_size")
+    return n.value
+
+
+def dca_prefill(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
+                workspace_bytes, stream=None):
+    _check(lib().dca_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), seq, C, W, rope_base,
+                             yarn_scale, _ref(mask), ctypes.byref(shape), _ptr(workspace), workspace_bytes,
+                             _stream(stream)), "dca_prefill")
+
+
+def dca_remap(q, k, v, seq, C, W, rope_base, shape, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_remap(_ptr(q), _ptr(k), _ptr(v), seq, C, W, rope_base, ctypes.byref(shape),
+                           _ptr(workspace), workspace_bytes, _stream(stream)), "dca_remap")
+
+
+def dca_vs_index(seq, C, W, mask, shape, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_vs_index(seq, C, W, _ref(mask), ctypes.byref(shape), _ptr(workspace), workspace_bytes,
+                              _stream(stream)), "dca_vs_index")
+
+
+def dca_attention(out, lse, seq, C, W, yarn_scale, mask, shape, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_attention(_ptr(out), _ptr(lse), seq, C, W, yarn_scale, _ref(mask), ctypes.byref(shape),
+                               _ptr(workspace), workspace_bytes, _stream(stream)), "dca_attention")
+
+
+def dca_debug_positions(seq, C, W, pq_intra, pq_succ, pq_inter, pk, stream=None):
+    _check(lib().dca_debug_positions(seq, C, W, _ptr(pq_intra), _ptr(pq_succ), _ptr(pq_inter), _ptr(pk),
+                                     _stream(stream)), "dca_debug_positions")
+
+
+def dca_debug_tile_regions(seq, C, out, stream=None):
+    _check(lib().dca_debug_tile_regions(seq, C, _ptr(out), _stream(stream)), "dca_debug_tile_regions")
+
+
+def dca_debug_unpack(workspace, workspace_bytes, which, seq, C, W, shape, dst, stream=None):
+    _check(lib().dca_debug_unpack(_ptr(workspace), workspace_bytes, which, seq, C, W, ctypes.byref(shape),
+                                  _ptr(dst), _stream(stream)), "dca_debug_unpack")
+
+
+def dca_debug_vs_lists(workspace, workspace_bytes, seq, C, W, mask, shape, vt, vt_count, dl, dl_count,
+                       stream=None):
+    _check(lib().dca_debug_vs_lists(_ptr(workspace), workspace_bytes, seq, C, W, _ref(mask), ctypes.byref(shape),
+                                    _ptr(vt), _ptr(vt_count), _ptr(dl), _ptr(dl_count), _stream(stream)),
+           "dca_debug_vs_lists")
+
+
+# ---- convenience --------------------------------------------------------------
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device byte buffer of at least nbytes."""
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def yarn_logit_scale(seq: int, C: int) -> float:
+    """The YaRN-style logit temperature max(1, 0.1 ln(seq / C) + 1)
+    [mizuki, DCA + YaRN]."""
+    return max(1.0, 0.1 * math.log(seq / C) + 1.0)
+
+
+def prefill(q, k, v, C: int, W: int, rope_base: float = 1e7, yarn_scale: float = 1.0,
+            vertical=None, slash=None, return_lse: bool = False, softmax_scale: float = 0.0,
+            workspace: torch.Tensor | None = None):
+    """DCA prefill on torch device tensors q [B, Hq, S, d], k and v [B, Hkv, S, d]
+    (contiguous, one dtype); optional vertical [Hq, nv] / slash [Hq, ns] int32
+    device tensors. Returns out (and lse) allocated with torch; the call is
+    enqueued on the current stream."""
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous")
+    seq = q.shape[2]
+    shape = shape_of(q, k, softmax_scale)
+    mask = make_mask(vertical, slash)
+    nbytes = dca_workspace_size(seq, C, W, shape, mask)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = alloc_workspace(nbytes, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    dca_prefill(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
+                workspace.numel())
+    return (out, lse) if return_lse else out

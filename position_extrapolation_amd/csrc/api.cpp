@@ -1,0 +1,336 @@
+// libdca C ABI: argument validation, derived constants, workspace layout and
+// stage sequencing. Every argument is checked before the first HIP call; a
+// rejected call enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "dca_internal.h"
+
+namespace dca {
+
+static thread_local std::string g_last_error;
+
+static int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+static int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+static int ok() {
+    g_last_error.clear();
+    return DCA_OK;
+}
+
+static int device_fail(int err, const char *what) {
+    return fail(DCA_E_DEVICE, "%s: HIP error %d (%s)", what, err, hip_error_text(err));
+}
+
+const char *hip_error_text(int err) { return hipGetErrorString((hipError_t)err); }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool misaligned(const void *ptr, uintptr_t a) { return ptr != nullptr && ((uintptr_t)ptr & (a - 1)) != 0; }
+
+Layout layout_for(const Problem &p) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    L.table = take((size_t)p.n_pos * (size_t)(p.D / 2) * 8);
+    const size_t qbytes = (size_t)p.B * p.Hq * p.S_pad * p.D * p.esize;
+    const size_t kvbytes = (size_t)p.B * p.Hkv * p.S_pad * p.D * p.esize;
+    for (int i = 0; i < 3; ++i) L.q[i] = take(qbytes);
+    L.k = take(kvbytes);
+    L.v = take(kvbytes);
+    if (p.sparse) {
+        L.vs_flags = take((size_t)2 * p.Hq * p.n_tiles);
+        L.vs_vt = take((size_t)p.Hq * p.n_tiles * 4);
+        L.vs_vt_n = take((size_t)p.Hq * 4);
+        L.vs_dl = take((size_t)p.Hq * p.n_tiles * 4);
+        L.vs_dl_n = take((size_t)p.Hq * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+// Validate sizes and the shape; fill p. Pointers are checked by callers.
+static int make_problem(int64_t seq, int64_t C, int64_t W, const dca_shape *shape,
+                        const dca_vs_mask *mask, Problem *p) {
+    if (shape == nullptr) return fail(DCA_E_INVALID, "shape is NULL");
+    if (seq < 1) return fail(DCA_E_INVALID, "seq must be >= 1 (got %lld)", (long long)seq);
+    if (seq >= ((int64_t)1 << 31)) return fail(DCA_E_UNSUPPORTED, "seq must be < 2^31");
+    if (C < 1 || W < 0) return fail(DCA_E_INVALID, "need C >= 1 and W >= 0 (got C=%lld W=%lld)",
+                                    (long long)C, (long long)W);
+    if (C < kTile || C % kTile != 0)
+        return fail(DCA_E_UNSUPPORTED, "C must be a positive multiple of %d (got %lld)", kTile, (long long)C);
+    if (W > C) return fail(DCA_E_UNSUPPORTED, "W must be <= C (got W=%lld C=%lld)", (long long)W, (long long)C);
+    if (C + W >= ((int64_t)1 << 31)) return fail(DCA_E_UNSUPPORTED, "C + W must be < 2^31");
+    if (shape->batch < 1 || shape->n_q_heads < 1 || shape->n_kv_heads < 1)
+        return fail(DCA_E_INVALID, "batch and head counts must be >= 1");
+    if (shape->n_q_heads % shape->n_kv_heads != 0)
+        return fail(DCA_E_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                    shape->n_q_heads, shape->n_kv_heads);
+    if (shape->head_dim != 64 && shape->head_dim != 128)
+        return fail(DCA_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", shape->head_dim);
+    if (shape->dtype != DCA_F32 && shape->dtype != DCA_BF16)
+        return fail(DCA_E_INVALID, "dtype must be DCA_F32 or DCA_BF16 (got %d)", shape->dtype);
+    if (!(shape->softmax_scale >= 0.f) || !isfinite(shape->softmax_scale))
+        return fail(DCA_E_INVALID, "softmax_scale must be finite and >= 0");
+    Problem q{};
+    q.B = shape->batch;
+    q.Hq = shape->n_q_heads;
+    q.Hkv = shape->n_kv_heads;
+    q.G = q.Hq / q.Hkv;
+    q.D = shape->head_dim;
+    q.S = seq;
+    q.S_pad = (seq + kSeqPad - 1) / kSeqPad * kSeqPad;
+    q.C = C;
+    q.W = W;
+    q.p_inter = C + W - 1;
+    q.n_pos = C + W;
+    q.n_tiles = (seq + kTile - 1) / kTile;
+    q.dtype = shape->dtype;
+    q.esize = shape->dtype == DCA_BF16 ? 2 : 4;
+    q.softmax_scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.f / sqrtf((float)q.D);
+    if (q.B * q.Hq * q.S_pad * q.D >= ((int64_t)1 << 40))
+        return fail(DCA_E_UNSUPPORTED, "problem too large");
+    if (mask != nullptr) {
+        if (mask->n_vertical < 0 || mask->n_slash < 0)
+            return fail(DCA_E_INVALID, "mask counts must be >= 0");
+        if (mask->n_vertical > 0 && mask->vertical == nullptr)
+            return fail(DCA_E_INVALID, "mask->vertical is NULL");
+        if (mask->n_slash > 0 && mask->slash == nullptr)
+            return fail(DCA_E_INVALID, "mask->slash is NULL");
+        if (misaligned(mask->vertical, 4) || misaligned(mask->slash, 4))
+            return fail(DCA_E_INVALID, "mask lists must be 4-byte aligned");
+        q.sparse = true;
+        q.n_vertical = mask->n_vertical;
+        q.n_slash = mask->n_slash;
+    }
+    *p = q;
+    return DCA_OK;
+}
+
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+static int check_workspace(const Problem &p, const void *ws, size_t bytes, Layout *L) {
+    *L = layout_for(p);
+    if (ws == nullptr) return fail(DCA_E_INVALID, "workspace is NULL");
+    if (((uintptr_t)ws & 255) != 0) return fail(DCA_E_INVALID, "workspace must be 256-byte aligned");
+    if (bytes < L->total)
+        return fail(DCA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, L->total);
+    return DCA_OK;
+}
+
+}  // namespace dca
+
+using namespace dca;
+
+extern "C" {
+
+const char *dca_status_str(int status) {
+    switch (status) {
+        case DCA_OK: return "DCA_OK";
+        case DCA_E_INVALID: return "DCA_E_INVALID: invalid argument";
+        case DCA_E_UNSUPPORTED: return "DCA_E_UNSUPPORTED: outside the supported domain";
+        case DCA_E_WORKSPACE: return "DCA_E_WORKSPACE: workspace too small";
+        case DCA_E_DEVICE: return "DCA_E_DEVICE: HIP runtime or launch failure";
+        default: return "unknown dca_status";
+    }
+}
+
+const char *dca_last_error(void) { return g_last_error.c_str(); }
+
+int dca_remap_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
+                        int32_t *pq_inter, int32_t *pk) {
+    if (seq < 1 || seq >= ((int64_t)1 << 31)) return fail(DCA_E_INVALID, "seq out of range");
+    if (C < 1 || W < 0 || C + W >= ((int64_t)1 << 31)) return fail(DCA_E_INVALID, "C or W out of range");
+    for (int64_t i = 0; i < seq; ++i) {
+        if (pq_intra) pq_intra[i] = (int32_t)pos_intra(i, C);
+        if (pq_succ) pq_succ[i] = (int32_t)pos_succ(i, C, W);
+        if (pk) pk[i] = (int32_t)pos_key(i, C);
+    }
+    if (pq_inter) *pq_inter = (int32_t)pos_inter(C, W);
+    return ok();
+}
+
+int dca_workspace_size(int64_t seq, int64_t C, int64_t W, const dca_shape *shape, const dca_vs_mask *mask,
+                       size_t *bytes) {
+    if (bytes == nullptr) return fail(DCA_E_INVALID, "bytes is NULL");
+    Problem p;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    *bytes = layout_for(p).total;
+    return ok();
+}
+
+static int check_rope(double rope_base) {
+    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(DCA_E_INVALID, "rope_base must be finite and > 1");
+    return DCA_OK;
+}
+
+static int check_yarn(float yarn_scale) {
+    if (!(yarn_scale > 0.f) || !isfinite(yarn_scale)) return fail(DCA_E_INVALID, "yarn_scale must be finite and > 0");
+    return DCA_OK;
+}
+
+static int do_remap(const Problem &p, const void *q, const void *k, const void *v, double rope_base, void *ws,
+                    const Layout &L, void *stream) {
+    int err = launch_rope_table(p, rope_base, ws, L, stream);
+    if (err) return device_fail(err, "rope table launch");
+    err = launch_remap(p, q, k, v, ws, L, stream);
+    if (err) return device_fail(err, "remap launch");
+    return DCA_OK;
+}
+
+int dca_remap(const void *q, const void *k, const void *v, int64_t seq, int64_t C, int64_t W, double rope_base,
+              const dca_shape *shape, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, nullptr, &p);
+    if (st) return st;
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    if ((st = do_remap(p, q, k, v, rope_base, workspace, L, stream))) return st;
+    return ok();
+}
+
+int dca_vs_index(int64_t seq, int64_t C, int64_t W, const dca_vs_mask *mask, const dca_shape *shape,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    Layout L;
+    if (mask == nullptr) return fail(DCA_E_INVALID, "mask is NULL");
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const int err = launch_vs_index(p, *mask, workspace, L, stream);
+    if (err) return device_fail(err, "vertical-slash index launch");
+    return ok();
+}
+
+static int check_outputs(const Problem &p, const void *out, const float *lse, const void *const *inputs,
+                         int n_inputs, const void *ws, size_t ws_bytes) {
+    if (out == nullptr) return fail(DCA_E_INVALID, "out is NULL");
+    if (misaligned(out, 16) || misaligned(lse, 4)) return fail(DCA_E_INVALID, "out must be 16-byte and lse 4-byte aligned");
+    const size_t obytes = (size_t)p.B * p.Hq * p.S * p.D * p.esize;
+    const size_t kvbytes = (size_t)p.B * p.Hkv * p.S * p.D * p.esize;
+    const size_t lbytes = lse ? (size_t)p.B * p.Hq * p.S * 4 : 0;
+    for (int i = 0; i < n_inputs; ++i) {
+        const size_t ib = i == 0 ? obytes : kvbytes;   // q first, then k, v
+        if (overlaps(out, obytes, inputs[i], ib)) return fail(DCA_E_INVALID, "out overlaps an input");
+        if (overlaps(lse, lbytes, inputs[i], ib)) return fail(DCA_E_INVALID, "lse overlaps an input");
+    }
+    if (overlaps(out, obytes, ws, ws_bytes)) return fail(DCA_E_INVALID, "out overlaps the workspace");
+    if (overlaps(lse, lbytes, ws, ws_bytes)) return fail(DCA_E_INVALID, "lse overlaps the workspace");
+    if (overlaps(lse, lbytes, out, obytes)) return fail(DCA_E_INVALID, "lse overlaps out");
+    return DCA_OK;
+}
+
+int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W, float yarn_scale,
+                  const dca_vs_mask *mask, const dca_shape *shape, const void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    if ((st = check_outputs(p, out, lse, nullptr, 0, workspace, workspace_bytes))) return st;
+    const int err = launch_attention(p, yarn_scale, out, lse, workspace, L, stream);
+    if (err) return device_fail(err, "attention launch");
+    return ok();
+}
+
+int dca_prefill(const void *q, const void *k, const void *v, void *out, float *lse, int64_t seq, int64_t C,
+                int64_t W, double rope_base, float yarn_scale, const dca_vs_mask *mask, const dca_shape *shape,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const void *inputs[3] = {q, k, v};
+    if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = do_remap(p, q, k, v, rope_base, workspace, L, stream))) return st;
+    if (p.sparse) {
+        const int err = launch_vs_index(p, *mask, workspace, L, stream);
+        if (err) return device_fail(err, "vertical-slash index launch");
+    }
+    const int err = launch_attention(p, yarn_scale, out, lse, workspace, L, stream);
+    if (err) return device_fail(err, "attention launch");
+    return ok();
+}
+
+int dca_debug_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
+                        int32_t *pq_inter, int32_t *pk, void *stream) {
+    if (seq < 1 || seq >= ((int64_t)1 << 31)) return fail(DCA_E_INVALID, "seq out of range");
+    if (C < 1 || W < 0 || C + W >= ((int64_t)1 << 31)) return fail(DCA_E_INVALID, "C or W out of range");
+    if (!pq_intra || !pq_succ || !pq_inter || !pk) return fail(DCA_E_INVALID, "output arrays must be non-NULL");
+    const int err = launch_debug_positions(seq, C, W, pq_intra, pq_succ, pq_inter, pk, stream);
+    if (err) return device_fail(err, "positions launch");
+    return ok();
+}
+
+int dca_debug_tile_regions(int64_t seq, int64_t C, uint8_t *out, void *stream) {
+    if (seq < 1 || seq > ((int64_t)1 << 22)) return fail(DCA_E_INVALID, "seq out of range for a region table");
+    if (C < kTile || C % kTile != 0) return fail(DCA_E_UNSUPPORTED, "C must be a positive multiple of 64");
+    if (out == nullptr) return fail(DCA_E_INVALID, "out is NULL");
+    const int err = launch_debug_tile_regions(seq, C, out, stream);
+    if (err) return device_fail(err, "tile-region launch");
+    return ok();
+}
+
+int dca_debug_unpack(const void *workspace, size_t workspace_bytes, int which, int64_t seq, int64_t C, int64_t W,
+                     const dca_shape *shape, void *dst, void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, nullptr, &p);
+    if (st) return st;
+    if (which < 0 || which > 4) return fail(DCA_E_INVALID, "which must be 0..4");
+    if (dst == nullptr) return fail(DCA_E_INVALID, "dst is NULL");
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const int err = launch_debug_unpack(p, workspace, L, which, dst, stream);
+    if (err) return device_fail(err, "unpack launch");
+    return ok();
+}
+
+int dca_debug_vs_lists(const void *workspace, size_t workspace_bytes, int64_t seq, int64_t C, int64_t W,
+                       const dca_vs_mask *mask, const dca_shape *shape, int32_t *vt, int32_t *vt_count,
+                       int32_t *dl, int32_t *dl_count, void *stream) {
+    Problem p;
+    Layout L;
+    if (mask == nullptr) return fail(DCA_E_INVALID, "mask is NULL");
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if (!vt || !vt_count || !dl || !dl_count) return fail(DCA_E_INVALID, "output arrays must be non-NULL");
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const int err = launch_debug_vs_lists(p, workspace, L, vt, vt_count, dl, dl_count, stream);
+    if (err) return device_fail(err, "list copy launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point include/dca.h declares, computes the host position map bit-exactly
+against the oracle, sizes the workspace, and rejects bad arguments before any
+HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from oracle import dca_oracle as O
+from position_extrapolation_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dca.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dca_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _declared()
+    assert len(names) >= 12
+    L = api.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(api.EXPORTS) == names
+
+
+@pytest.mark.parametrize("S,C,W", [(20, 8, 3), (2048, 512, 128), (1000, 64, 0), (777, 128, 128),
+                                   (131072, 32768, 4096)])
+def test_host_positions_bit_exact(S, C, W):
+    pqi, pqs, pinter, pk = api.dca_remap_positions(S, C, W)
+    oi, os_, op = O.query_positions(S, C, W)
+    assert torch.equal(pqi.to(torch.int64), oi)
+    assert torch.equal(pqs.to(torch.int64), os_)
+    assert pinter == op
+    assert torch.equal(pk.to(torch.int64), O.key_positions(S, C))
+
+
+def test_workspace_size_formula():
+    sh = api.make_shape(1, 28, 4, 128, torch.bfloat16)
+    S, C, W = 32768, 8192, 1024
+    n = api.dca_workspace_size(S, C, W, sh)
+    q = 28 * S * 128 * 2
+    kv = 4 * S * 128 * 2
+    table = (C + W) * 64 * 8
+    assert n >= 3 * q + 2 * kv + table
+    assert n <= 3 * q + 2 * kv + table + 6 * 256
+    m = api.dca_vs_mask(None, None, 0, 0)
+    assert api.dca_workspace_size(S, C, W, sh, m) > n
+
+
+def _call_prefill(**over):
+    sh = over.pop("shape", api.make_shape(1, 2, 1, 64, torch.float32))
+    args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, seq=2048, C=512,
+                W=128, base=1e7, yarn=1.0, mask=None, ws=0x50000000, ws_bytes=1 << 30)
+    args.update(over)
+    L = api.lib()
+    return L.dca_prefill(args["q"], args["k"], args["v"], args["out"], args["lse"], args["seq"], args["C"],
+                         args["W"], args["base"], args["yarn"],
+                         None if args["mask"] is None else ctypes.byref(args["mask"]), ctypes.byref(sh),
+                         args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.DCA_E_INVALID),
+    (dict(out=None), api.DCA_E_INVALID),
+    (dict(seq=0), api.DCA_E_INVALID),
+    (dict(C=100), api.DCA_E_UNSUPPORTED),
+    (dict(C=0), api.DCA_E_INVALID),
+    (dict(W=-1), api.DCA_E_INVALID),
+    (dict(W=600), api.DCA_E_UNSUPPORTED),
+    (dict(base=1.0), api.DCA_E_INVALID),
+    (dict(base=float("nan")), api.DCA_E_INVALID),
+    (dict(yarn=0.0), api.DCA_E_INVALID),
+    (dict(yarn=float("inf")), api.DCA_E_INVALID),
+    (dict(ws=None), api.DCA_E_INVALID),
+    (dict(ws=0x50000010), api.DCA_E_INVALID),
+    (dict(ws_bytes=1000), api.DCA_E_WORKSPACE),
+    (dict(out=0x10000000), api.DCA_E_INVALID),            # out aliases q
+    (dict(out=0x50000000 + 4096), api.DCA_E_INVALID),     # out inside the workspace
+    (dict(lse=0x40000000 + 100), api.DCA_E_INVALID),      # lse inside out
+    (dict(shape=api.make_shape(1, 3, 2, 64, torch.float32)), api.DCA_E_INVALID),
+    (dict(shape=api.make_shape(1, 2, 1, 96, torch.float32)), api.DCA_E_UNSUPPORTED),
+    (dict(shape=api.make_shape(0, 2, 1, 64, torch.float32)), api.DCA_E_INVALID),
+    (dict(shape=api.dca_shape(1, 2, 1, 64, 7, 0.0)), api.DCA_E_INVALID),
+    (dict(shape=api.dca_shape(1, 2, 1, 64, 0, -1.0)), api.DCA_E_INVALID),
+    (dict(mask=api.dca_vs_mask(None, None, 5, 0)), api.DCA_E_INVALID),
+    (dict(mask=api.dca_vs_mask(None, None, -1, 0)), api.DCA_E_INVALID),
+    (dict(seq=1 << 31), api.DCA_E_UNSUPPORTED),
+])
+def test_invalid_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_prefill(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_prefill() == api.DCA_E_DEVICE
+    assert "HIP error" in api.dca_last_error()
+
+
+def test_status_strings():
+    for s in range(5):
+        assert api.dca_status_str(s).startswith("DCA_")
+    assert api.dca_status_str(99) == "unknown dca_status"

@@ -1,0 +1,360 @@
+"""GPU parity of libdca against the CPU oracle (MI355X).
+
+Every case prints what it runs before touching the GPU. Outputs are compared
+element by element with the float64 oracle on the same seeded inputs:
+max-abs <= 1e-4 for fp32 and <= 2e-2 for bf16, plus, for bf16, a
+discrimination guard (the error must be far below how much a wrong position
+mapping would move the output) and planted needles. Position maps, tile
+regions and vertical-slash tile lists are compared bit-exactly.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dca_oracle as O
+from position_extrapolation_amd import api, synth, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _wl(name, **over):
+    w = workloads.get(name)
+    return workloads.Workload(**{**w.__dict__, **over})
+
+
+def _run(q, k, v, w, vertical=None, slash=None, lse=True):
+    out, l = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, vertical=vertical,
+                         slash=slash, return_lse=True)
+    torch.cuda.synchronize()
+    return out, l
+
+
+def _oracle(q, k, v, rows, w, vertical=None, slash=None, query_pos=None):
+    rows_t = torch.as_tensor(rows, dtype=torch.int64)
+    q_rows = q[:, :, rows_t.to(q.device)].cpu()
+    return O.dca_prefill_rows(q_rows, rows_t, k.cpu(), v.cpu(), w.chunk, w.window, w.rope_base,
+                              w.yarn_scale, vertical=vertical, slash=slash, query_pos=query_pos)
+
+
+def _err(gpu_rows, ref):
+    return (gpu_rows.double().cpu() - ref).abs().max().item()
+
+
+# ---------------------------------------------------------------------------
+# integer stages: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,C,W", [(2048, 512, 128), (1000, 64, 0), (131072, 32768, 4096),
+                                   (1048576, 262144, 32768), (777, 128, 128)])
+def test_device_positions_bit_exact(S, C, W):
+    say(f"[positions] S={S} C={C} W={W}")
+    pqi = torch.empty(S, dtype=torch.int32, device=DEV)
+    pqs = torch.empty_like(pqi)
+    pk = torch.empty_like(pqi)
+    pin = torch.empty(1, dtype=torch.int32, device=DEV)
+    api.dca_debug_positions(S, C, W, pqi, pqs, pin, pk)
+    torch.cuda.synchronize()
+    oi, os_, op = O.query_positions(S, C, W)
+    assert torch.equal(pqi.cpu().long(), oi)
+    assert torch.equal(pqs.cpu().long(), os_)
+    assert int(pin.item()) == op
+    assert torch.equal(pk.cpu().long(), O.key_positions(S, C))
+
+
+@pytest.mark.parametrize("S,C", [(2048, 512), (1000, 64), (4096, 1024), (777, 128)])
+def test_device_tile_regions_bit_exact(S, C):
+    say(f"[tile regions] S={S} C={C}")
+    n = (S + 63) // 64
+    out = torch.empty(n * n, dtype=torch.uint8, device=DEV)
+    api.dca_debug_tile_regions(S, C, out)
+    torch.cuda.synchronize()
+    t = torch.arange(n)[:, None].expand(n, n)
+    kt = torch.arange(n)[None, :].expand(n, n)
+    # every pair of a tile has the region of the tile's first pair
+    ref = O.pair_region(64 * t, 64 * kt, C)
+    for di, dj in [(63, 0), (0, 63), (63, 63)]:
+        ii = torch.clamp(64 * t + di, max=S - 1)
+        jj = torch.clamp(64 * kt + dj, max=S - 1)
+        other = O.pair_region(ii, jj, C)
+        assert torch.equal(other[kt < t], ref[kt < t])
+    ref = torch.where(kt > t, torch.full_like(ref, 255), ref)
+    assert torch.equal(out.cpu().long().view(n, n), ref)
+
+
+# ---------------------------------------------------------------------------
+# remap pre-pass values
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D,S,C,W", [("bf16", 128, 1000, 256, 64), ("f32", 64, 2048, 512, 128),
+                                           ("bf16", 64, 300, 64, 64), ("f32", 128, 513, 128, 0)])
+def test_remap_prepass_matches_oracle_rotation(dtype, D, S, C, W):
+    say(f"[remap] dtype={dtype} D={D} S={S} C={C} W={W}")
+    w = workloads.Workload("t", 1, 4, 2, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=3, device=DEV)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_workspace_size(S, C, W, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    api.dca_remap(q, k, v, S, C, W, w.rope_base, shape, ws, nbytes)
+    outs = []
+    for which in range(5):
+        dst = torch.empty_like(q if which < 3 else k)
+        api.dca_debug_unpack(ws, nbytes, which, S, C, W, shape, dst)
+        outs.append(dst)
+    torch.cuda.synchronize()
+    pqi, pqs, pin = O.query_positions(S, C, W)
+    ref_q = [O.rope_rotate(q.cpu(), pqi, w.rope_base), O.rope_rotate(q.cpu(), pqs, w.rope_base),
+             O.rope_rotate(q.cpu(), torch.full((S,), pin), w.rope_base)]
+    ref_k = O.rope_rotate(k.cpu(), O.key_positions(S, C), w.rope_base)
+    for got, ref in zip(outs[:3] + [outs[3]], ref_q + [ref_k]):
+        g = got.double().cpu()
+        if dtype == "bf16":
+            # one bf16 rounding of a float32 result: relative 2^-8 plus fp32 slack
+            assert ((g - ref).abs() <= ref.abs() * 2.0 ** -8 + 1e-5).all()
+        else:
+            assert (g - ref).abs().max().item() <= 1e-5
+    assert torch.equal(outs[4], v)
+
+
+# ---------------------------------------------------------------------------
+# attention parity
+# ---------------------------------------------------------------------------
+
+def test_parity_tiny_f32_all_rows():
+    w = workloads.get("tiny_2k_f32")
+    say(f"[parity] {w.name} all rows")
+    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    out, lse = _run(q, k, v, w)
+    rows = np.arange(w.seq)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err = _err(out, ref)
+    lerr = _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["f32"]
+    assert lerr <= TOL["f32"]
+    van, _ = O.vanilla_prefill_rows(q.cpu(), torch.arange(w.seq), k.cpu(), v.cpu(), w.rope_base, 1.0)
+    assert (van - ref).abs().max().item() > 100 * err
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,S,C,W", [
+    ("bf16", 4, 2, 128, 1000, 256, 64),     # ragged tail, 4 chunks
+    ("bf16", 3, 1, 64, 777, 128, 128),      # W = C, d = 64, G = 3
+    ("bf16", 2, 2, 128, 640, 64, 0),        # W = 0, C = 64, no GQA
+    ("f32", 4, 1, 128, 515, 128, 32),       # fp32, d = 128
+    ("f32", 2, 1, 64, 65, 64, 16),          # one row past a chunk
+    ("bf16", 2, 1, 128, 1, 64, 8),          # a single row
+    ("bf16", 2, 1, 128, 4096, 4096, 100),   # C = S: plain causal RoPE
+])
+def test_parity_small_all_rows(dtype, Hq, Hkv, D, S, C, W):
+    say(f"[parity] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W}")
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=11, device=DEV)
+    out, lse = _run(q, k, v, w)
+    ref, ref_lse = _oracle(q, k, v, np.arange(S), w)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL[dtype]
+    assert lerr <= (1e-4 if dtype == "f32" else 2e-2)
+    if dtype == "bf16":
+        # far tighter than the bound: one bf16 rounding of the output (relative
+        # 2^-9, doubled) plus the bf16 rounding of q, k and P inside the sum
+        g = out.double().cpu()
+        assert ((g - ref).abs() <= ref.abs() * 2.0 ** -8 + 2e-3).all()
+
+
+def _discrimination(q, k, v, rows, w, ref, gpu_rows):
+    """The GPU error must sit far below how far two wrong position mappings
+    move the output: vanilla RoPE, and successive-chunk pairs treated as
+    inter-chunk. Measured on the rows past the first chunk -- the only rows
+    DCA changes -- where outputs are small and the bf16 output rounding does
+    not mask a wrong mapping."""
+    far = torch.as_tensor(rows >= w.chunk)
+    pqi, pqs, pin = O.query_positions(w.seq, w.chunk, w.window)
+    wrong_succ, _ = _oracle(q, k, v, rows, w, query_pos=(pqi, torch.full_like(pqs, pin), pin))
+    rows_t = torch.as_tensor(rows)
+    van, _ = O.vanilla_prefill_rows(q[:, :, rows_t.to(q.device)].cpu(), rows_t, k.cpu(), v.cpu(),
+                                    w.rope_base, w.yarn_scale)
+    d1 = (van - ref)[:, :, far].abs().max().item()
+    d2 = (wrong_succ - ref)[:, :, far].abs().max().item()
+    err = (gpu_rows.double().cpu() - ref)[:, :, far].abs().max().item()
+    say(f"  rows >= C: wrong-mapping distances vanilla={d1:.3e} succ-as-inter={d2:.3e}; gpu err={err:.3e}")
+    assert err <= 0.1 * min(d1, d2)
+
+
+@pytest.mark.parametrize("name", ["qwen7b_32k", "qwen7b_128k"])
+def test_parity_sampled_rows(name):
+    w = workloads.get(name)
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, w.oracle_rows, seed=0)
+    say(f"[parity] {name}: {len(rows)} sampled rows x {w.n_q_heads} heads")
+    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    out, lse = _run(q, k, v, w)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    err = _err(out[:, :, rows_t], ref)
+    lerr = _err(lse[:, :, rows_t], ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    _discrimination(q, k, v, rows, w, ref, out[:, :, rows_t])
+
+
+def test_planted_needles_bf16():
+    """For chosen rows, overwrite one key so that its rotated copy is a large
+    multiple of the row's rotated query under the pair's region; the output of
+    that row must then be close to the needle's value row."""
+    w = _wl("qwen7b_32k", n_q_heads=4, n_kv_heads=1)
+    say(f"[needles] S={w.seq} C={w.chunk} W={w.window}")
+    q, k, v = synth.make_qkv(w, seed=5, device=DEV)
+    S, C, W = w.seq, w.chunk, w.window
+    pqi, pqs, pin = O.query_positions(S, C, W)
+    pk = O.key_positions(S, C)
+    cases = [  # (row, key, position variant of the pair)
+        (C + 3, C - 5, pqs),            # successive, inside the window
+        (2 * C + W + 10, C + 7, pqs),   # successive, pinned
+        (3 * C + 5, 100, None),         # inter
+        (2 * C + 500, 2 * C + 200, pqi),  # intra
+    ]
+    kc = k.cpu().clone()
+    h = 0
+    for i, j, var in cases:
+        qpos = torch.tensor([pin]) if var is None else var[i:i + 1]
+        rq = O.rope_rotate(q[0, h, i:i + 1].cpu(), qpos, w.rope_base)
+        alpha = 20.0 / (w.yarn_scale * rq.norm().item() ** 2 / math.sqrt(w.head_dim))
+        kc[0, 0, j] = O.rope_rotate(alpha * rq, -pk[j:j + 1], w.rope_base)[0].to(k.dtype)
+    k2 = kc.to(DEV)
+    out, _ = _run(q, k2, v, w)
+    rows = np.array([c[0] for c in cases])
+    ref, _ = _oracle(q, k2, v, rows, w)
+    for n, (i, j, _) in enumerate(cases):
+        got = out[0, h, i].double().cpu()
+        target = v[0, 0, j].double().cpu()
+        say(f"  row {i} key {j}: |gpu - v_j|={(got - target).abs().max():.3e} "
+            f"|oracle - v_j|={(ref[0, h, n] - target).abs().max():.3e}")
+        assert (ref[0, h, n] - target).abs().max() < 0.05
+        assert (got - target).abs().max() < 0.06
+    err = _err(out[:, :, torch.as_tensor(rows, device=DEV)], ref)
+    assert err <= TOL["bf16"]
+
+
+def test_deterministic_and_writes_every_output():
+    w = _wl("qwen7b_32k", seq=5000, chunk=1024, window=128)
+    say(f"[determinism] S={w.seq}")
+    q, k, v = synth.make_qkv(w, seed=2, device=DEV)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), device=DEV)
+        api.dca_prefill(q, k, v, out, lse, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, None,
+                        shape, ws, nbytes)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_workspace_too_small_leaves_output_untouched():
+    w = _wl("qwen7b_32k", seq=1024, chunk=256, window=64)
+    q, k, v = synth.make_qkv(w, seed=2, device=DEV)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(api.DcaError) as e:
+        api.dca_prefill(q, k, v, out, None, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, None,
+                        shape, ws, nbytes - 1)
+    assert e.value.status == api.DCA_E_WORKSPACE
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+def test_stages_equal_prefill():
+    w = _wl("qwen7b_32k", seq=3000, chunk=512, window=64)
+    q, k, v = synth.make_qkv(w, seed=4, device=DEV)
+    ref = _run(q, k, v, w)[0]
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    out = torch.empty_like(q)
+    api.dca_remap(q, k, v, w.seq, w.chunk, w.window, w.rope_base, shape, ws, nbytes)
+    api.dca_attention(out, None, w.seq, w.chunk, w.window, w.yarn_scale, None, shape, ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+# ---------------------------------------------------------------------------
+# vertical-slash sparse path
+# ---------------------------------------------------------------------------
+
+def _vs_case(w, seed=0):
+    vert, slash = synth.vs_mask(w.n_q_heads, w.seq, w.n_vertical, w.n_slash, seed=seed)
+    return torch.from_numpy(vert), torch.from_numpy(slash)
+
+
+@pytest.mark.parametrize("S,nv,ns", [(4096, 40, 60), (1000, 70, 70), (131072, 1000, 2000)])
+def test_vs_index_lists_bit_exact(S, nv, ns):
+    say(f"[vs index] S={S} nv={nv} ns={ns}")
+    w = _wl("qwen14b_1m_vs", seq=S, chunk=1024 if S >= 1024 else 64, window=64, n_vertical=nv, n_slash=ns,
+            n_q_heads=8, n_kv_heads=2)
+    vert, slash = _vs_case(w, seed=9)
+    shape = api.make_shape(1, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    mask = api.make_mask(vd, sd)
+    nbytes = api.dca_workspace_size(S, w.chunk, w.window, shape, mask)
+    ws = api.alloc_workspace(nbytes, DEV)
+    api.dca_vs_index(S, w.chunk, w.window, mask, shape, ws, nbytes)
+    nt = (S + 63) // 64
+    vt = torch.empty((w.n_q_heads, nt), dtype=torch.int32, device=DEV)
+    dl = torch.empty_like(vt)
+    vn = torch.empty(w.n_q_heads, dtype=torch.int32, device=DEV)
+    dn = torch.empty_like(vn)
+    api.dca_debug_vs_lists(ws, nbytes, S, w.chunk, w.window, mask, shape, vt, vn, dl, dn)
+    torch.cuda.synchronize()
+    for h in range(w.n_q_heads):
+        rvt, rdl = O.vs_tile_lists(vert[h], slash[h], S)
+        assert int(vn[h]) == len(rvt) and int(dn[h]) == len(rdl)
+        assert torch.equal(vt[h, :len(rvt)].cpu().long(), rvt)
+        assert torch.equal(dl[h, :len(rdl)].cpu().long(), rdl)
+
+
+@pytest.mark.parametrize("S,C,W,nv,ns", [(4096, 1024, 128, 40, 60), (1000, 256, 64, 10, 12),
+                                         (32768, 8192, 1024, 300, 600)])
+def test_vs_parity(S, C, W, nv, ns):
+    say(f"[vs parity] S={S} C={C} W={W} nv={nv} ns={ns}")
+    w = _wl("qwen14b_1m_vs", seq=S, chunk=C, window=W, n_vertical=nv, n_slash=ns, n_q_heads=4,
+            n_kv_heads=1)
+    q, k, v = synth.make_qkv(w, seed=1, device=DEV)
+    vert, slash = _vs_case(w, seed=1)
+    out, lse = _run(q, k, v, w, vertical=vert.to(DEV), slash=slash.to(DEV))
+    rows = synth.sample_rows(S, C, W, None if S <= 4096 else 512, seed=1)
+    ref, ref_lse = _oracle(q, k, v, rows, w, vertical=vert, slash=slash)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    err, lerr = _err(out[:, :, rows_t], ref), _err(lse[:, :, rows_t], ref_lse)
+    dense, _ = _oracle(q, k, v, rows, w)
+    dd = (dense - ref).abs().max().item()
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}; dense-vs-sparse distance {dd:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    assert err <= 0.1 * dd
