@@ -7,6 +7,7 @@
 namespace dca {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -26,6 +27,16 @@ struct Frag<__bf16> {
     __device__ static inline void mma(const vec &a, const vec &b, f32x16 &c) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // acc + sum of the 8 elements (two-element dot products with ones)
+    __device__ static inline float sum_into(const vec &v, float acc) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+        }
+        return acc;
+    }
 };
 
 // f32: four v_mfma_f32_32x32x2_f32 per fragment; op t takes element t of
@@ -42,6 +53,7 @@ struct Frag<float> {
 #pragma unroll
         for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], c, 0, 0, 0);
     }
+    __device__ static inline float sum_into(const vec &v, float acc) { return acc + ((v[0] + v[1]) + (v[2] + v[3])); }
 };
 
 }  // namespace dca
