@@ -110,16 +110,16 @@ class Runner:
         w = self.w
         if events is not None:
             events[0].record()
-        api.dca_remap(self.q, self.k, self.v, w.seq, w.chunk, w.window, w.rope_base, self.shape, self.ws,
-                      self.nbytes)
+        api.dca_remap(self.q, self.k, self.v, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, self.shape,
+                      self.ws, self.nbytes)
         if events is not None:
             events[1].record()
         if self.mask is not None:
             api.dca_vs_index(w.seq, w.chunk, w.window, self.mask, self.shape, self.ws, self.nbytes)
         if events is not None:
             events[2].record()
-        api.dca_attention(self.out, self.lse, w.seq, w.chunk, w.window, w.yarn_scale, self.mask, self.shape,
-                          self.ws, self.nbytes)
+        api.dca_attention(self.out, self.lse, w.seq, w.chunk, w.window, self.mask, self.shape, self.ws,
+                          self.nbytes)
         if events is not None:
             events[3].record()
 

@@ -131,9 +131,11 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
 /* The three stages of dca_prefill, callable one at a time on the same
  * workspace (for per-stage timing and checks):
  *   dca_remap      -- the RoPE/DCA pre-pass: writes the cos/sin table, the
- *                     three rotated query variants, the rotated keys and the
- *                     value re-layout into the workspace [mizuki, Inter-Chunk:
- *                     only position indices change].
+ *                     three rotated query variants, the rotated keys (scaled
+ *                     by yarn_scale * softmax_scale * log2(e), so that scores
+ *                     come out of the matrix cores in base-2 exponent units)
+ *                     and the value re-layout into the workspace [mizuki,
+ *                     Inter-Chunk: only position indices change].
  *   dca_vs_index   -- mask -> per-head sorted key-tile list VT_h (tiles
  *                     holding a vertical column) and tile-distance list D_h
  *                     (distances delta < ceil(seq/64) whose slash interval
@@ -143,16 +145,17 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
  *                     dca_remap (and dca_vs_index when mask != NULL).
  * Arguments have the meaning they have in dca_prefill; each stage validates
  * them the same way. dca_attention needs the same seq, C, W, shape and mask
- * as the dca_remap / dca_vs_index calls that filled the workspace. */
+ * as the dca_remap / dca_vs_index calls that filled the workspace (the YaRN
+ * temperature is applied by dca_remap). */
 int dca_remap(const void *q, const void *k, const void *v,
-              int64_t seq, int64_t C, int64_t W, double rope_base,
+              int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale,
               const dca_shape *shape, void *workspace, size_t workspace_bytes,
               void *stream);
 int dca_vs_index(int64_t seq, int64_t C, int64_t W, const dca_vs_mask *mask,
                  const dca_shape *shape, void *workspace, size_t workspace_bytes,
                  void *stream);
 int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W,
-                  float yarn_scale, const dca_vs_mask *mask, const dca_shape *shape,
+                  const dca_vs_mask *mask, const dca_shape *shape,
                   const void *workspace, size_t workspace_bytes, void *stream);
 
 /* Checks (device): read back what the GPU stages computed.
@@ -167,7 +170,7 @@ int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W,
  * dca_debug_unpack -- copy one pre-pass array out of a workspace filled by
  *   dca_remap, in plain row-major [batch, heads, seq, head_dim] order and the
  *   shape's dtype: which = 0 Q intra, 1 Q successive, 2 Q inter (n_q_heads),
- *   3 rotated K, 4 V (n_kv_heads). dst: device.
+ *   3 rotated K (scaled as dca_remap states), 4 V (n_kv_heads). dst: device.
  * dca_debug_vs_lists -- copy the tile lists dca_vs_index wrote: vt and dl
  *   are device int32 [n_q_heads][n_tiles] (n_tiles = ceil(seq/64)), counts
  *   device int32 [n_q_heads] each. */

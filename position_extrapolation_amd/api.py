@@ -54,11 +54,10 @@ _SIGS = {
     "dca_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
     "dca_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double,
                                    ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
-    "dca_remap": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double, _VP, _VP,
+    "dca_remap": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float, _VP, _VP,
                                  ctypes.c_size_t, _VP]),
     "dca_vs_index": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
-    "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, ctypes.c_float, _VP, _VP, _VP,
-                                     ctypes.c_size_t, _VP]),
+    "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_debug_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "dca_debug_tile_regions": (ctypes.c_int, [_I64, _I64, _VP, _VP]),
     "dca_debug_unpack": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _I64, _I64, _I64, _VP, _VP, _VP]),
@@ -160,8 +159,8 @@ def dca_prefill(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape
                              _stream(stream)), "dca_prefill")
 
 
-def dca_remap(q, k, v, seq, C, W, rope_base, shape, workspace, workspace_bytes, stream=None):
-    _check(lib().dca_remap(_ptr(q), _ptr(k), _ptr(v), seq, C, W, rope_base, ctypes.byref(shape),
+def dca_remap(q, k, v, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_remap(_ptr(q), _ptr(k), _ptr(v), seq, C, W, rope_base, yarn_scale, ctypes.byref(shape),
                            _ptr(workspace), workspace_bytes, _stream(stream)), "dca_remap")
 
 
@@ -170,8 +169,8 @@ def dca_vs_index(seq, C, W, mask, shape, workspace, workspace_bytes, stream=None
                               _stream(stream)), "dca_vs_index")
 
 
-def dca_attention(out, lse, seq, C, W, yarn_scale, mask, shape, workspace, workspace_bytes, stream=None):
-    _check(lib().dca_attention(_ptr(out), _ptr(lse), seq, C, W, yarn_scale, _ref(mask), ctypes.byref(shape),
+def dca_attention(out, lse, seq, C, W, mask, shape, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_attention(_ptr(out), _ptr(lse), seq, C, W, _ref(mask), ctypes.byref(shape),
                                _ptr(workspace), workspace_bytes, _stream(stream)), "dca_attention")
 
 

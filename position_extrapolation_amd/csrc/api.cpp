@@ -190,17 +190,18 @@ static int check_yarn(float yarn_scale) {
     return DCA_OK;
 }
 
-static int do_remap(const Problem &p, const void *q, const void *k, const void *v, double rope_base, void *ws,
-                    const Layout &L, void *stream) {
+static int do_remap(const Problem &p, const void *q, const void *k, const void *v, double rope_base,
+                    float yarn_scale, void *ws, const Layout &L, void *stream) {
     int err = launch_rope_table(p, rope_base, ws, L, stream);
     if (err) return device_fail(err, "rope table launch");
-    err = launch_remap(p, q, k, v, ws, L, stream);
+    const float k_scale = yarn_scale * p.softmax_scale * 1.4426950408889634f;
+    err = launch_remap(p, q, k, v, k_scale, ws, L, stream);
     if (err) return device_fail(err, "remap launch");
     return DCA_OK;
 }
 
 int dca_remap(const void *q, const void *k, const void *v, int64_t seq, int64_t C, int64_t W, double rope_base,
-              const dca_shape *shape, void *workspace, size_t workspace_bytes, void *stream) {
+              float yarn_scale, const dca_shape *shape, void *workspace, size_t workspace_bytes, void *stream) {
     Problem p;
     Layout L;
     int st = make_problem(seq, C, W, shape, nullptr, &p);
@@ -209,8 +210,9 @@ int dca_remap(const void *q, const void *k, const void *v, int64_t seq, int64_t 
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
         return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
     if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
-    if ((st = do_remap(p, q, k, v, rope_base, workspace, L, stream))) return st;
+    if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     return ok();
 }
 
@@ -245,17 +247,15 @@ static int check_outputs(const Problem &p, const void *out, const float *lse, co
     return DCA_OK;
 }
 
-int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W, float yarn_scale,
-                  const dca_vs_mask *mask, const dca_shape *shape, const void *workspace, size_t workspace_bytes,
-                  void *stream) {
+int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W, const dca_vs_mask *mask,
+                  const dca_shape *shape, const void *workspace, size_t workspace_bytes, void *stream) {
     Problem p;
     Layout L;
     int st = make_problem(seq, C, W, shape, mask, &p);
     if (st) return st;
-    if ((st = check_yarn(yarn_scale))) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
     if ((st = check_outputs(p, out, lse, nullptr, 0, workspace, workspace_bytes))) return st;
-    const int err = launch_attention(p, yarn_scale, out, lse, workspace, L, stream);
+    const int err = launch_attention(p, out, lse, workspace, L, stream);
     if (err) return device_fail(err, "attention launch");
     return ok();
 }
@@ -275,12 +275,12 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
     const void *inputs[3] = {q, k, v};
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
-    if ((st = do_remap(p, q, k, v, rope_base, workspace, L, stream))) return st;
+    if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     if (p.sparse) {
         const int err = launch_vs_index(p, *mask, workspace, L, stream);
         if (err) return device_fail(err, "vertical-slash index launch");
     }
-    const int err = launch_attention(p, yarn_scale, out, lse, workspace, L, stream);
+    const int err = launch_attention(p, out, lse, workspace, L, stream);
     if (err) return device_fail(err, "attention launch");
     return ok();
 }

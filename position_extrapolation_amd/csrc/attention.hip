@@ -43,7 +43,6 @@ struct AttnArgs {
     float *lse;
     int64_t S, C;
     int32_t Hq, Hkv, G, nblk;
-    float ks;                 // tau * sigma * log2(e)
     // work decode
     int32_t n_rt, KVH, s_split, M, per_xcd;
     // vertical-slash lists
@@ -53,10 +52,6 @@ struct AttnArgs {
 };
 
 constexpr int kNone = 0x7fffffff;
-// A row's running max is raised (and O rescaled) only when a new tile's max
-// exceeds it by more than this many powers of two; until then scores are
-// exponentiated against the stale max, which bounds every P by 2^8.
-constexpr float kLazyRescale = 8.0f;
 
 __device__ inline float lane_swap32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -137,7 +132,6 @@ struct TileIter {
 struct WaveCtx {
     int lane, x, gsel, wave, r0, tb_succ, tb_intra, wave_qt;
     bool active_rows;
-    float ks;
     int64_t qbase;               // element offset of this wave's 32-row block in a Q variant
     const char *kbytes, *vbytes; // this KV head's fragment-ordered K and V
 };
@@ -170,131 +164,6 @@ __device__ __forceinline__ void dma_tile(const WaveCtx &c, const char *base, int
     }
 }
 
-// Registers one wave carries across key tiles.
-template <typename T, int D>
-struct WaveState {
-    using vec = typename Frag<T>::vec;
-    static constexpr int NU = D / (2 * Frag<T>::E);
-    static constexpr int NDB = D / 32;
-    vec qfrag[NU];
-    int region;
-    f32x16 oacc[NDB];
-    float m_ref;   // reference max of raw scores (this row); raised lazily
-    float l_run;   // sum of 2^((s - m_ref) ks) over this lane's keys
-};
-
-template <typename T, int D>
-__device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, WaveState<T, D> &st, int region) {
-    using vec = typename Frag<T>::vec;
-    if (region == st.region) return;
-    const vec *qs = (const vec *)a.qf[region] + c.qbase / Frag<T>::E;
-#pragma unroll
-    for (int u = 0; u < WaveState<T, D>::NU; ++u) st.qfrag[u] = qs[u * 64 + c.lane];
-    st.region = region;
-    // land them here (twice per row block at most): no compiler-counted load
-    // is then outstanding while tile loads are in flight
-    __builtin_amdgcn_s_waitcnt(0);
-}
-
-// S^T (64 keys x 32 rows) = K_rot Q^T: two 32-key blocks.
-template <typename T, int D>
-__device__ __forceinline__ void qk(const WaveCtx &c, const WaveState<T, D> &st, const char *__restrict__ kl,
-                                   f32x16 (&s)[2]) {
-    using F = Frag<T>;
-    using vec = typename F::vec;
-    constexpr int NU = WaveState<T, D>::NU;
-    const vec *k = (const vec *)kl;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int u = 0; u < NU; ++u) F::mma(k[(kb * NU + u) * 64 + c.lane], st.qfrag[u], s[kb]);
-    }
-}
-
-// Causal mask of the tile that holds this wave's diagonal (keys past the row).
-__device__ __forceinline__ void mask_diag(const WaveCtx &c, int j0, f32x16 (&s)[2]) {
-    const int lim = c.r0 + c.x - j0 - 4 * c.gsel;     // key offset k is kept iff k <= lim
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            if (kBlk * kb + 8 * (v / 4) + (v % 4) > lim) s[kb][v] = -INFINITY;
-}
-
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    return mx;
-}
-
-// Raise the reference max when the tile's row max exceeds it by more than
-// 2^kLazyRescale (always on a row's first tile), rescaling O and l.
-template <typename T, int D>
-__device__ __forceinline__ void maybe_raise(const WaveCtx &c, WaveState<T, D> &st, float mx) {
-    mx = fmaxf(mx, lane_swap32(mx));
-    const bool raise = (mx - st.m_ref) * c.ks > kLazyRescale;   // true while m_ref = -inf
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = fmaxf(st.m_ref, mx);
-        const float alpha = __builtin_amdgcn_exp2f((st.m_ref - m_new) * c.ks);   // 0 on a first tile
-        st.l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < WaveState<T, D>::NDB; ++db) st.oacc[db] *= alpha;
-        st.m_ref = m_new;
-    }
-}
-
-// P = 2^(s ks + neg) rounded to the operand type, in PV fragment order, with
-// neg = -m_ref ks (or -inf: P = 0); the row sum of the rounded P is added to l.
-template <typename T, int D>
-__device__ __forceinline__ void softmax_p(const WaveCtx &c, WaveState<T, D> &st, const f32x16 (&s)[2], float neg,
-                                          typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
-    using F = Frag<T>;
-    constexpr int E = F::E;
-    constexpr int NUV = kBlk / (2 * E);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            F::set(p[kb][v / E], v % E, F::from_float(__builtin_amdgcn_exp2f(fmaf(s[kb][v], c.ks, neg))));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < NUV; ++u) st.l_run = F::sum_into(p[kb][u], st.l_run);
-}
-
-// O^T += V^T P^T
-template <typename T, int D>
-__device__ __forceinline__ void pv(const WaveCtx &c, WaveState<T, D> &st, const char *__restrict__ vlds,
-                                   const typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
-    using F = Frag<T>;
-    using vec = typename F::vec;
-    constexpr int NDB = WaveState<T, D>::NDB;
-    constexpr int NUV = kBlk / (2 * F::E);
-    const vec *vl = (const vec *)vlds;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < NUV; ++u) F::mma(vl[((kb * NDB + db) * NUV + u) * 64 + c.lane], p[kb][u], st.oacc[db]);
-}
-
-// Tile pipeline window: kt_n .. kt_{n+NS} with their query-tile masks (-1
-// past the end), whether this wave works on kt_n, and how many loads this
-// wave issued in the previous step (still in flight at the next step's top).
-template <int NS>
-struct Pipe {
-    int t[NS + 1];
-    unsigned m[NS + 1];
-    int n;
-    int prev_loads;
-    bool act0;
-};
-
 // s_waitcnt vmcnt(N) (expcnt, lgkmcnt not waited), gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -311,93 +180,133 @@ __device__ __forceinline__ int region_of_tile(const WaveCtx &c, int kt) {
 // the one tile of a wave that can hold keys past its rows
 __device__ __forceinline__ bool is_diag(const WaveCtx &c, int kt) { return kt * kTile + kTile - 1 > c.r0; }
 
-// Instruction order of one fused step (bf16, d = 128): two LDS reads run
-// ahead; each of the 16 QK^T matrix ops is followed by a share of the
-// softmax VALU work (exp2, bf16 packing, row sums) and the LDS read two ops
-// ahead, so the matrix cores and the VALU stay busy together; the 16 PV ops
-// follow with their V reads. Masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read.
-template <typename T, int D>
-__device__ __forceinline__ void interleave_step() {
-    if constexpr (sizeof(T) == 2 && D == 128) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+// Causal mask of the tile that holds this wave's diagonal (keys past the row).
+__device__ __forceinline__ void mask_diag(const WaveCtx &c, int j0, f32x16 (&s)[2]) {
+    const int lim = c.r0 + c.x - j0 - 4 * c.gsel;     // key offset k is kept iff k <= lim
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    }
+        for (int v = 0; v < 16; ++v)
+            if (kBlk * kb + 8 * (v / 4) + (v % 4) > lim) s[kb][v] = -INFINITY;
 }
 
-// Step n of the pipeline over an NS-slot ring for K and one for V (tile
-// kt_j lives in slot j mod NS): wait until K(kt_{n+1}) and V(kt_n) have
-// landed (loads of the last NS - 2 steps may stay in flight), start K of
-// kt_{n+NS} and V of kt_{n+NS-1}, mask and take the row max of kt_n, then
-// the scores of kt_{n+1} on the matrix cores alongside the softmax of kt_n
-// on the VALU, and the PV of kt_n.
-// The block is the same whether or not this wave works on kt_n and kt_{n+1}
-// (a tile past a wave's diagonal, an inactive vertical-slash tile, the last
-// step): inactive work is neutralised instead of skipped -- P of an inactive
-// kt_n is exactly 0 (exponent offset -inf), and an inactive kt_{n+1} is
-// neither masked nor used for the reference max -- so the hot block has no
-// data-dependent branches besides the rare max raise and query reload.
-template <typename T, int D, int NW, int NS, int NT>
-__device__ __forceinline__ void pipe_step(const AttnArgs &a, const WaveCtx &c, WaveState<T, D> &st,
-                                          TileIter<NT> &it, Pipe<NS> &pp, const char *lds, uint32_t lds_base,
-                                          f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+// Registers one wave carries across key tiles.
+template <typename T, int D>
+struct WaveState {
     using vec = typename Frag<T>::vec;
-    constexpr int NUV = kBlk / (2 * Frag<T>::E);
-    constexpr int TILE_BYTES = 2 * kBlk * D * (int)sizeof(T);
-    constexpr int STEP_LOADS = 2 * (TILE_BYTES / 1024 / NW);   // per wave: one K and one V tile share
-    if constexpr (NS >= 3) {
-        if (pp.prev_loads == STEP_LOADS) wait_vmcnt<STEP_LOADS>(); else __builtin_amdgcn_s_waitcnt(0);
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();                    // every wave's loads landed; the slots refilled below are free
-    const bool has1 = pp.t[1] >= 0;
-    const bool act1 = has1 && active(c, pp.t[1], pp.m[1]);
-    if (has1) load_q(a, c, st, region_of_tile(c, pp.t[1]));
-    // LDS: K slots at [0, NS TILE_BYTES), V slots at [NS TILE_BYTES, 2 NS TILE_BYTES)
-    int loads = 0;
-    if (pp.t[NS] >= 0) {
-        dma_tile<T, D, NW>(c, c.kbytes, pp.t[NS], lds_base + ((pp.n + NS) % NS) * TILE_BYTES);
-        loads += STEP_LOADS / 2;
-    }
-    if (pp.t[NS - 1] >= 0) {
-        dma_tile<T, D, NW>(c, c.vbytes, pp.t[NS - 1], lds_base + (NS + (pp.n + NS - 1) % NS) * TILE_BYTES);
-        loads += STEP_LOADS / 2;
-    }
-    pp.prev_loads = loads;
-    const char *klds_next = lds + ((pp.n + 1) % NS) * TILE_BYTES;
-    const char *vlds_cur = lds + (NS + pp.n % NS) * TILE_BYTES;
+    static constexpr int NU = D / (2 * Frag<T>::E);
+    static constexpr int NDB = D / 32;
+    vec qfrag[NU];
+    int region;
+    bool first;    // no tile of this row block seen yet (reference max unset)
+    f32x16 oacc[NDB];
+    float mref;    // reference max of the row's scores (base-2 exponent units)
+    float l_run;   // sum of 2^(s - mref) over this lane's keys
+};
 
-    // kt_n: causal mask if it holds the diagonal, then its row max (and a
-    // rare raise of the reference max) before its P is formed
-    if (pp.act0) {
-        if (is_diag(c, pp.t[0])) mask_diag(c, pp.t[0] * kTile, s_cur);
-        maybe_raise(c, st, tile_max(s_cur));
-    }
-    vec p[2][NUV];
-    const float neg = pp.act0 ? -st.m_ref * c.ks : -INFINITY;
-    qk<T, D>(c, st, klds_next, s_next);
-    softmax_p(c, st, s_cur, neg, p);
-    pv<T, D>(c, st, vlds_cur, p);
-    interleave_step<T, D>();
-
-    pp.act0 = act1;
+template <typename T, int D>
+__device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, WaveState<T, D> &st, int region) {
+    using vec = typename Frag<T>::vec;
+    if (region == st.region) return;
+    const vec *qs = (const vec *)a.qf[region] + c.qbase / Frag<T>::E;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        pp.t[i] = pp.t[i + 1];
-        pp.m[i] = pp.m[i + 1];
-    }
-    pp.t[NS] = pp.t[NS] >= 0 ? it.next(pp.m[NS]) : -1;
-    ++pp.n;
+    for (int u = 0; u < WaveState<T, D>::NU; ++u) st.qfrag[u] = qs[u * 64 + c.lane];
+    st.region = region;
+    // land them here (twice per row block at most): no compiler-counted load
+    // is then outstanding while tile loads are in flight
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// The pre-pass scales the rotated keys by yarn * sigma * log2 e, so the
+// matrix cores deliver scores s in base-2 exponent units. Each 32x32 score
+// accumulator starts at -mref (every value of a lane belongs to the lane's
+// row), so it ends as s - mref and P = 2^(s - mref) needs no further
+// arithmetic. Masked pairs hold -inf (P = 0).
+//
+// The row max is not taken on the common path. mref is only a reference: P
+// stays exact whatever its value as long as nothing overflows, so a tile is
+// accepted when every lane's sum of P over its 32 keys is finite and at most
+// 2^20 (then every P <= 2^20). Otherwise -- and on a row block's first tile --
+// the exact tile max is taken, mref raised to it (O and l rescaled), and P
+// recomputed.
+constexpr float kPsumLimit = 1048576.0f;   // 2^20
+
+template <typename T, int D>
+__device__ __forceinline__ void tile_scores(const WaveCtx &c, const WaveState<T, D> &st, const char *__restrict__ kl,
+                                            f32x16 (&s)[2]) {
+    using F = Frag<T>;
+    using vec = typename F::vec;
+    constexpr int NU = WaveState<T, D>::NU;
+    const vec *k = (const vec *)kl;
+    const float init = st.first ? 0.f : -st.mref;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = init;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) F::mma(k[(kb * NU + u) * 64 + c.lane], st.qfrag[u], s[kb]);
+}
+
+// P = 2^s rounded to the operand type, in PV fragment order; returns this
+// lane's sum of the rounded P.
+template <typename T>
+__device__ __forceinline__ float tile_p(const f32x16 (&s)[2], typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
+    using F = Frag<T>;
+    constexpr int E = F::E;
+    constexpr int NUV = kBlk / (2 * E);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) F::set(p[kb][v / E], v % E, F::from_float(__builtin_amdgcn_exp2f(s[kb][v])));
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < NUV; ++u) sum = F::sum_into(p[kb][u], sum);
+    return sum;
+}
+
+// Raise mref to the tile's row max (or set it on the first tile), shift the
+// scores to the new reference and rescale O and l.
+template <typename T, int D>
+__device__ __forceinline__ void raise_ref(WaveState<T, D> &st, f32x16 (&s)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, lane_swap32(mx));
+    // rows of an active wave always hold a finite score in every tile they visit
+    const float d = st.first ? mx : fmaxf(mx, 0.f);
+    const float alpha = st.first ? 0.f : __builtin_amdgcn_exp2f(-d);
+    st.mref = (st.first ? 0.f : st.mref) + d;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] -= d;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < WaveState<T, D>::NDB; ++db) st.oacc[db] *= alpha;
+    st.first = false;
+}
+
+// O^T += V^T P^T
+template <typename T, int D>
+__device__ __forceinline__ void tile_pv(const WaveCtx &c, WaveState<T, D> &st, const char *__restrict__ vlds,
+                                        const typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
+    using F = Frag<T>;
+    using vec = typename F::vec;
+    constexpr int NDB = WaveState<T, D>::NDB;
+    constexpr int NUV = kBlk / (2 * F::E);
+    const vec *vl = (const vec *)vlds;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < NUV; ++u)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) F::mma(vl[((kb * NDB + db) * NUV + u) * 64 + c.lane], p[kb][u], st.oacc[db]);
 }
 
 template <typename T, int D, int NW, int NS>
@@ -412,11 +321,12 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     constexpr int NT = BM / kTile;             // 64-row query tiles per workgroup
     constexpr int BLK_ELEMS = kBlk * D;
     constexpr int TILE_BYTES = 2 * BLK_ELEMS * (int)sizeof(T);   // one 64-key tile of K (or V)
+    constexpr int STEP_LOADS = 2 * (TILE_BYTES / 1024 / NW);     // per wave and step: its share of K and V
     static_assert(NT >= 1 && BM % kTile == 0, "workgroup rows must cover whole 64-row tiles");
+    static_assert(NS == 2 || NS == 3, "two or three ring slots");
 
-    // LDS: a ring of NS K tiles and a ring of NS V tiles. K runs one tile
-    // ahead of V: while tile n's P meets V(n), tile n+1's scores are formed
-    // from K(n+1); loads of the next NS - 1 tiles are in flight.
+    // LDS: NS slots, each [K tile | V tile]. Key tile kt_j lives in slot
+    // j mod NS; tiles kt_{n+1} .. kt_{n+NS-1} are in flight while kt_n is used.
     extern __shared__ __attribute__((aligned(1024))) char lds_dyn[];
     char *lds = lds_dyn;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
@@ -459,67 +369,73 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     c.tb_intra = cq * tiles_per_chunk;
     c.tb_succ = cq >= 1 ? c.tb_intra - tiles_per_chunk : 0;
     c.wave_qt = (kBlk * wave) / kTile;
-    c.ks = a.ks;
     c.qbase = (bh * a.nblk + c.r0 / kBlk) * (int64_t)BLK_ELEMS;
     c.kbytes = (const char *)a.kf + bkv * a.nblk * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
     c.vbytes = (const char *)a.vf + bkv * a.nblk * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
 
     WaveState<T, D> st;
     st.region = -1;
+    st.first = true;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
-    st.m_ref = -INFINITY;
+    st.mref = 0.f;
     st.l_run = 0.f;
 
-    // ---- pipeline prologue ---------------------------------------------------
+    // ---- tile window and prologue ---------------------------------------------
     TileIter<NT> it;
     it.init(a, h, i0, S, last_row / kTile);
-    Pipe<NS> pp;
-    pp.t[0] = it.next(pp.m[0]);
+    int t[NS];                       // kt_n .. kt_{n+NS-1}
+    unsigned m[NS];
 #pragma unroll
-    for (int i = 1; i <= NS; ++i) {
-        pp.m[i] = 0;
-        pp.t[i] = pp.t[i - 1] >= 0 ? it.next(pp.m[i]) : -1;
+    for (int i = 0; i < NS; ++i) {
+        m[i] = 0;
+        t[i] = (i == 0 || t[i - 1] >= 0) ? it.next(m[i]) : -1;
     }
-    pp.n = 0;
-    // slots: K(kt_j), V(kt_j) -> j mod NS. Step 0 needs K(kt_0), K(kt_1) and
-    // V(kt_0) landed; with three slots, K(kt_2) and V(kt_1) (the loads a step
-    // leaves in flight) may still be on their way.
-    static_assert(NS == 2 || NS == 3, "two or three ring slots");
-    constexpr int STEP_LOADS = 2 * (TILE_BYTES / 1024 / NW);
-    if (pp.t[0] >= 0) {
-        dma_tile<T, D, NW>(c, c.kbytes, pp.t[0], lds_base);
-        dma_tile<T, D, NW>(c, c.vbytes, pp.t[0], lds_base + NS * TILE_BYTES);
-    }
-    if (pp.t[1] >= 0) dma_tile<T, D, NW>(c, c.kbytes, pp.t[1], lds_base + TILE_BYTES);
-    pp.prev_loads = 0;
-    if constexpr (NS == 3) {
-        if (pp.t[2] >= 0) {
-            dma_tile<T, D, NW>(c, c.kbytes, pp.t[2], lds_base + 2 * TILE_BYTES);
-            pp.prev_loads += STEP_LOADS / 2;
-        }
-        if (pp.t[1] >= 0) {
-            dma_tile<T, D, NW>(c, c.vbytes, pp.t[1], lds_base + (NS + 1) * TILE_BYTES);
-            pp.prev_loads += STEP_LOADS / 2;
-        }
-        if (pp.prev_loads == STEP_LOADS) wait_vmcnt<STEP_LOADS>(); else __builtin_amdgcn_s_waitcnt(0);
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
-    f32x16 sa[2], sb[2];          // scores of the current and the next tile (roles alternate)
-    sa[0] = sa[1] = f32x16{};
-    pp.act0 = pp.t[0] >= 0 && active(c, pp.t[0], pp.m[0]);
-    if (pp.act0) {
-        load_q(a, c, st, region_of_tile(c, pp.t[0]));
-        qk<T, D>(c, st, lds, sa);
-    }
+    auto issue = [&](int kt, int j) __attribute__((always_inline)) {
+        const uint32_t slot_addr = lds_base + (uint32_t)(j % NS) * 2 * TILE_BYTES;
+        dma_tile<T, D, NW>(c, c.kbytes, kt, slot_addr);
+        dma_tile<T, D, NW>(c, c.vbytes, kt, slot_addr + TILE_BYTES);
+    };
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (t[i] >= 0) issue(t[i], i);
+    // step n waits for kt_n; the loads of kt_{n+1} .. kt_{n+NS-2} may stay in flight
+    int inflight = (NS == 3 && t[1] >= 0) ? STEP_LOADS : 0;
 
-    // ---- steady state: step n works on tiles kt_n and kt_{n+1} ---------------
-    while (pp.t[0] >= 0) {
-        pipe_step<T, D, NW, NS>(a, c, st, it, pp, lds, lds_base, sa, sb);
-        if (pp.t[0] < 0) break;
-        pipe_step<T, D, NW, NS>(a, c, st, it, pp, lds, lds_base, sb, sa);
+    // ---- main loop: one key tile per step ------------------------------------
+    for (int n = 0; t[0] >= 0; ++n) {
+        if (NS == 3 && inflight == STEP_LOADS) wait_vmcnt<STEP_LOADS>(); else __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                     // every wave's loads of kt_n landed; slot (n-1) mod NS is free
+        const int kt = t[0];
+        const bool act = active(c, kt, m[0]);
+        if (act) load_q(a, c, st, region_of_tile(c, kt));
+        if (t[NS - 1] >= 0) {
+            issue(t[NS - 1], n + NS - 1);
+            inflight = STEP_LOADS;
+        } else {
+            inflight = 0;
+        }
+        if (act) {
+            const char *cur = lds + (n % NS) * 2 * TILE_BYTES;
+            f32x16 s[2];
+            tile_scores<T, D>(c, st, cur, s);
+            if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
+            vec p[2][NUV];
+            float psum = tile_p<T>(s, p);
+            const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
+            if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
+                raise_ref<T, D>(st, s);
+                psum = tile_p<T>(s, p);
+            }
+            st.l_run += psum;
+            tile_pv<T, D>(c, st, cur + TILE_BYTES, p);
+        }
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i) {
+            t[i] = t[i + 1];
+            m[i] = m[i + 1];
+        }
+        t[NS - 1] = t[NS - 1] >= 0 ? it.next(m[NS - 1]) : -1;
     }
 
     // ---- epilogue -----------------------------------------------------------
@@ -537,8 +453,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
             for (int e = 0; e < 4; ++e) orow[d0 + e] = F::from_float(st.oacc[db][4 * vq + e] * inv);
         }
     if (a.lse != nullptr && c.gsel == 0) {
-        a.lse[bh * a.S + row] = l_tot > 0.f ? (st.m_ref * c.ks + log2f(l_tot)) * 0.69314718055994531f
-                                            : -INFINITY;
+        // natural log: (mref + log2 l) ln 2
+        a.lse[bh * a.S + row] = l_tot > 0.f ? (st.mref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
@@ -555,7 +471,7 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     const int64_t per_stream = (a.n_rt + a.s_split - 1) / a.s_split;
     a.per_xcd = (int32_t)(per_stream * a.M * a.G);
     const int64_t grid = (int64_t)a.per_xcd * kXcds;
-    const int lds_bytes = 2 * NS * (2 * kBlk * D * (int)sizeof(T));   // K and V rings of NS tiles
+    const int lds_bytes = NS * 2 * (2 * kBlk * D * (int)sizeof(T));   // NS slots of [K tile | V tile]
     auto kern = dca_attention_kernel<T, D, NW, NS>;
     if (lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -566,8 +482,7 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     return (int)hipGetLastError();
 }
 
-int launch_attention(const Problem &p, float yarn_scale, void *out, float *lse, const void *ws,
-                     const Layout &L, void *stream) {
+int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream) {
     AttnArgs a{};
     for (int i = 0; i < 3; ++i) a.qf[i] = (const char *)ws + L.q[i];
     a.kf = (const char *)ws + L.k;
@@ -580,7 +495,6 @@ int launch_attention(const Problem &p, float yarn_scale, void *out, float *lse, 
     a.Hkv = (int32_t)p.Hkv;
     a.G = (int32_t)p.G;
     a.nblk = (int32_t)(p.S_pad / kBlk);
-    a.ks = yarn_scale * p.softmax_scale * 1.4426950408889634f;
     a.KVH = (int32_t)(p.B * p.Hkv);
     a.sparse = p.sparse ? 1 : 0;
     if (p.sparse) {

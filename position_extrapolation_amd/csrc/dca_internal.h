@@ -85,11 +85,11 @@ __host__ __device__ inline int region_of(int64_t cq, int64_t ck) {
 
 // Launchers (return hipError_t as int; 0 = success).
 int launch_rope_table(const Problem &p, double rope_base, void *ws, const Layout &L, void *stream);
-int launch_remap(const Problem &p, const void *q, const void *k, const void *v, void *ws,
+// k_scale multiplies the rotated keys (yarn * softmax scale * log2 e)
+int launch_remap(const Problem &p, const void *q, const void *k, const void *v, float k_scale, void *ws,
                  const Layout &L, void *stream);
 int launch_vs_index(const Problem &p, const dca_vs_mask &m, void *ws, const Layout &L, void *stream);
-int launch_attention(const Problem &p, float yarn_scale, void *out, float *lse, const void *ws,
-                     const Layout &L, void *stream);
+int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream);
 int launch_debug_positions(int64_t S, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
                            int32_t *pq_inter, int32_t *pk, void *stream);
 int launch_debug_tile_regions(int64_t S, int64_t C, uint8_t *out, void *stream);

@@ -4,7 +4,9 @@
 // sit at j mod C, each query gets three positions (intra r(i), successive
 // min(C + r(i), C + W - 1), inter C + W - 1). This pass rotates every key once
 // and every query three times and writes the results, plus a re-laid-out copy
-// of V, in the attention kernel's fragment order (see dca_internal.h). It is
+// of V, in the attention kernel's fragment order (see dca_internal.h); the
+// rotated keys are scaled by yarn * softmax_scale * log2(e) so that scores
+// leave the matrix cores in base-2 exponent units [mizuki, DCA + YaRN]. It is
 // bound by HBM bandwidth: per token it reads (Hq + 2 Hkv) d elements and
 // writes (3 Hq + 2 Hkv) d elements.
 //
@@ -53,6 +55,7 @@ struct RemapArgs {
     void *qf[3];
     void *kf, *vf;
     const float2 *table;
+    float k_scale;               // multiplies the rotated keys
     int64_t S, C, W;
     int32_t Hq, Hkv, nblk;
 };
@@ -143,11 +146,12 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
             typename F::vec y1 = F::zero(), y2 = F::zero();
             if (valid) {
                 const float2 *cs = a.table + pos * HALF + c * E;
+                const float sc = is_q ? 1.f : a.k_scale;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float2 t = cs[e];
-                    F::set(y1, e, F::from_float(f1[e] * t.x - f2[e] * t.y));
-                    F::set(y2, e, F::from_float(f2[e] * t.x + f1[e] * t.y));
+                    F::set(y1, e, F::from_float((f1[e] * t.x - f2[e] * t.y) * sc));
+                    F::set(y2, e, F::from_float((f2[e] * t.x + f1[e] * t.y) * sc));
                 }
             }
             T *dst = (T *)(is_q ? a.qf[var] : a.kf) + (bh * a.nblk + blk) * BLK_ELEMS;
@@ -159,9 +163,10 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
 }
 
 template <typename T, int D>
-static int launch_remap_t(const Problem &p, const void *q, const void *k, const void *v, void *ws,
+static int launch_remap_t(const Problem &p, const void *q, const void *k, const void *v, float k_scale, void *ws,
                           const Layout &L, void *stream) {
     RemapArgs a{};
+    a.k_scale = k_scale;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -180,13 +185,13 @@ static int launch_remap_t(const Problem &p, const void *q, const void *k, const 
     return (int)hipGetLastError();
 }
 
-int launch_remap(const Problem &p, const void *q, const void *k, const void *v, void *ws,
+int launch_remap(const Problem &p, const void *q, const void *k, const void *v, float k_scale, void *ws,
                  const Layout &L, void *stream) {
     if (p.dtype == DCA_BF16)
-        return p.D == 128 ? launch_remap_t<__bf16, 128>(p, q, k, v, ws, L, stream)
-                          : launch_remap_t<__bf16, 64>(p, q, k, v, ws, L, stream);
-    return p.D == 128 ? launch_remap_t<float, 128>(p, q, k, v, ws, L, stream)
-                      : launch_remap_t<float, 64>(p, q, k, v, ws, L, stream);
+        return p.D == 128 ? launch_remap_t<__bf16, 128>(p, q, k, v, k_scale, ws, L, stream)
+                          : launch_remap_t<__bf16, 64>(p, q, k, v, k_scale, ws, L, stream);
+    return p.D == 128 ? launch_remap_t<float, 128>(p, q, k, v, k_scale, ws, L, stream)
+                      : launch_remap_t<float, 64>(p, q, k, v, k_scale, ws, L, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -117,7 +117,7 @@ def test_remap_prepass_matches_oracle_rotation(dtype, D, S, C, W):
     shape = api.shape_of(q, k)
     nbytes = api.dca_workspace_size(S, C, W, shape)
     ws = api.alloc_workspace(nbytes, DEV)
-    api.dca_remap(q, k, v, S, C, W, w.rope_base, shape, ws, nbytes)
+    api.dca_remap(q, k, v, S, C, W, w.rope_base, w.yarn_scale, shape, ws, nbytes)
     outs = []
     for which in range(5):
         dst = torch.empty_like(q if which < 3 else k)
@@ -127,7 +127,9 @@ def test_remap_prepass_matches_oracle_rotation(dtype, D, S, C, W):
     pqi, pqs, pin = O.query_positions(S, C, W)
     ref_q = [O.rope_rotate(q.cpu(), pqi, w.rope_base), O.rope_rotate(q.cpu(), pqs, w.rope_base),
              O.rope_rotate(q.cpu(), torch.full((S,), pin), w.rope_base)]
-    ref_k = O.rope_rotate(k.cpu(), O.key_positions(S, C), w.rope_base)
+    # the pre-pass scales the rotated keys by yarn * sigma * log2(e)
+    ks = w.yarn_scale / math.sqrt(D) * math.log2(math.e)
+    ref_k = O.rope_rotate(k.cpu(), O.key_positions(S, C), w.rope_base) * ks
     for got, ref in zip(outs[:3] + [outs[3]], ref_q + [ref_k]):
         g = got.double().cpu()
         if dtype == "bf16":
@@ -299,8 +301,8 @@ def test_stages_equal_prefill():
     nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, shape)
     ws = api.alloc_workspace(nbytes, DEV)
     out = torch.empty_like(q)
-    api.dca_remap(q, k, v, w.seq, w.chunk, w.window, w.rope_base, shape, ws, nbytes)
-    api.dca_attention(out, None, w.seq, w.chunk, w.window, w.yarn_scale, None, shape, ws, nbytes)
+    api.dca_remap(q, k, v, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, shape, ws, nbytes)
+    api.dca_attention(out, None, w.seq, w.chunk, w.window, None, shape, ws, nbytes)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
 
