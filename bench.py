@@ -191,6 +191,39 @@ def cpu_baseline(name, n_rows=8, seed=0):
                       f"heads, float64 torch-CPU oracle, {dt:.1f} s"}
 
 
+def measured_traffic(workload: str, kernel_key: str = ""):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (profiles/traffic.json, already scaled by the copy calibration), or
+    None when the kernel source has changed since they were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("traffic", {}).get(workload + kernel_key)
+    if rec is None:
+        return None
+    src = "remap.hip" if kernel_key == ":remap" else "attention.hip"
+    field = "remap_source_sha256_16" if kernel_key == ":remap" else "attention_source_sha256_16"
+    digest = hashlib.sha256(open(os.path.join(ROOT, "position_extrapolation_amd", "csrc", src), "rb").read())
+    if digest.hexdigest()[:16] != rec.get(field):
+        return None
+    return {"total": rec["read_bytes"] + rec["written_bytes"], "read": rec["read_bytes"],
+            "written": rec["written_bytes"]}
+
+
+def copy_calibration(mib: int, device):
+    """A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+    converts those counters into bytes for the attention kernel."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +232,9 @@ def main():
     ap.add_argument("--workload", default="qwen14b_1m")
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K and vertical-slash workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,8 +244,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    api.lib()
     dev = "cuda:0"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, dev)
+        return
+    api.lib()
 
     w, main_res = measure(args.workload, args.steps, args.warmup, dev)
     extra = []
@@ -222,6 +260,8 @@ def main():
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]
+    traffic = measured_traffic(w.name)
+    remap_traffic = measured_traffic(w.name, ":remap")
     result = {
         "metric": "DCA prefill attention TFLOP/s (1M tokens, Qwen2.5-14B layer shape, one MI355X)",
         "value": round(main_res["tflops"], 2),
@@ -241,10 +281,14 @@ def main():
                    "yarn_scale": round(w.yarn_scale, 10), "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * main_res["tflops"] / peak, 2),
         "roofline": {"kernel": "dca_attention_kernel", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if traffic is None else traffic["total"],
+                     "traffic_detail": traffic},
         "remap": {"kernel": "remap_kernel", "bound": "hbm", "ms": round(main_res["remap_ms"], 3),
                   "achieved": round(main_res["remap_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                  "frac": round(main_res["remap_gbs"] / PEAK_HBM_GBS, 4)},
+                  "frac": round(main_res["remap_gbs"] / PEAK_HBM_GBS, 4),
+                  "algorithmic_bytes": remap_bytes(w),
+                  "traffic": None if remap_traffic is None else remap_traffic["total"]},
         "attention_ms": round(main_res["attention_ms"], 3),
         "extra": extra,
     }
