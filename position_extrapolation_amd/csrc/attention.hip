@@ -10,8 +10,8 @@
 // reloading its query fragments twice at most.
 //
 // Per workgroup: NW waves x 32 query rows of one query head; 64-key K and V
-// tiles staged through LDS (double-buffered, one barrier per tile). Per wave
-// and tile:
+// tiles staged through an LDS ring, two tiles per barrier, the next two in
+// flight. Per wave and tile:
 //   S^T (64 keys x 32 rows) = K_rot Q_x^T     2 x (D/16) bf16 MFMA 32x32x16
 //   online softmax (exp2 domain, scale tau * sigma * log2 e); a lane holds 32
 //     scores of one row, the row max is completed with one lane swap
@@ -171,6 +171,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most `pending` (<= MAXP) tiles of SL loads each are in flight.
+template <int SL, int MAXP>
+__device__ __forceinline__ void wait_tiles(int pending) {
+    if constexpr (MAXP >= 3) if (pending == 3) { wait_vmcnt<3 * SL>(); return; }
+    if constexpr (MAXP >= 2) if (pending == 2) { wait_vmcnt<2 * SL>(); return; }
+    if constexpr (MAXP >= 1) if (pending == 1) { wait_vmcnt<SL>(); return; }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 __device__ __forceinline__ bool active(const WaveCtx &c, int kt, unsigned m) {
     return c.active_rows && kt * kTile <= c.r0 + kBlk - 1 && ((m >> c.wave_qt) & 1u);
 }
@@ -231,6 +240,9 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, Wave
 // recomputed.
 constexpr float kPsumLimit = 1048576.0f;   // 2^20
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
 template <typename T, int D>
 __device__ __forceinline__ void tile_scores(const WaveCtx &c, const WaveState<T, D> &st, const char *__restrict__ kl,
                                             f32x16 (&s)[2]) {
@@ -247,6 +259,19 @@ __device__ __forceinline__ void tile_scores(const WaveCtx &c, const WaveState<T,
     for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) F::mma(k[(kb * NU + u) * 64 + c.lane], st.qfrag[u], s[kb]);
+    if constexpr (sizeof(T) == 2) {
+        // schedule: the accumulator set-up, then K fragment reads kept
+        // AHEAD deep in front of the matrix-core ops that consume them
+        constexpr int N = 2 * NU, AHEAD = N < 4 ? N : 4;
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < N - AHEAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
+    }
 }
 
 // P = 2^s rounded to the operand type, in PV fragment order; returns this
@@ -292,24 +317,41 @@ __device__ __forceinline__ void raise_ref(WaveState<T, D> &st, f32x16 (&s)[2]) {
     st.first = false;
 }
 
-// O^T += V^T P^T
+// V^T fragments of one tile, in the order the PV loop consumes them: read
+// from LDS while the softmax runs.
 template <typename T, int D>
-__device__ __forceinline__ void tile_pv(const WaveCtx &c, WaveState<T, D> &st, const char *__restrict__ vlds,
-                                        const typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
-    using F = Frag<T>;
-    using vec = typename F::vec;
-    constexpr int NDB = WaveState<T, D>::NDB;
-    constexpr int NUV = kBlk / (2 * F::E);
+struct VFrags {
+    typename Frag<T>::vec v[2][kBlk / (2 * Frag<T>::E)][D / 32];
+};
+template <typename T, int D>
+__device__ __forceinline__ void load_v(const WaveCtx &c, const char *__restrict__ vlds, VFrags<T, D> &vf) {
+    using vec = typename Frag<T>::vec;
+    constexpr int NDB = D / 32;
+    constexpr int NUV = kBlk / (2 * Frag<T>::E);
     const vec *vl = (const vec *)vlds;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < NUV; ++u)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) F::mma(vl[((kb * NDB + db) * NUV + u) * 64 + c.lane], p[kb][u], st.oacc[db]);
+            for (int db = 0; db < NDB; ++db) vf.v[kb][u][db] = vl[((kb * NDB + db) * NUV + u) * 64 + c.lane];
+}
+// O^T += V^T P^T
+template <typename T, int D>
+__device__ __forceinline__ void tile_pv(WaveState<T, D> &st, const VFrags<T, D> &vf,
+                                             const typename Frag<T>::vec (&p)[2][kBlk / (2 * Frag<T>::E)]) {
+    using F = Frag<T>;
+    constexpr int NDB = D / 32;
+    constexpr int NUV = kBlk / (2 * F::E);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < NUV; ++u)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) F::mma(vf.v[kb][u][db], p[kb][u], st.oacc[db]);
 }
 
-template <typename T, int D, int NW, int NS>
+template <typename T, int D, int NW, int NS, int TPS>
 // second bound: at least two waves per SIMD (256 registers per wave)
 __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     using F = Frag<T>;
@@ -323,10 +365,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     constexpr int TILE_BYTES = 2 * BLK_ELEMS * (int)sizeof(T);   // one 64-key tile of K (or V)
     constexpr int STEP_LOADS = 2 * (TILE_BYTES / 1024 / NW);     // per wave and step: its share of K and V
     static_assert(NT >= 1 && BM % kTile == 0, "workgroup rows must cover whole 64-row tiles");
-    static_assert(NS == 2 || NS == 3, "two or three ring slots");
 
-    // LDS: NS slots, each [K tile | V tile]. Key tile kt_j lives in slot
-    // j mod NS; tiles kt_{n+1} .. kt_{n+NS-1} are in flight while kt_n is used.
     extern __shared__ __attribute__((aligned(1024))) char lds_dyn[];
     char *lds = lds_dyn;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
@@ -382,9 +421,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     st.l_run = 0.f;
 
     // ---- tile window and prologue ---------------------------------------------
+    // A step handles TPS key tiles between two barriers. LDS holds a ring of NS
+    // slots of [K tile | V tile]; tile j (in visiting order) lives in slot
+    // j mod NS. Step n uses tiles nTPS .. nTPS+TPS-1 and, once every wave is
+    // past the barrier that frees the slots of step n-1, starts the loads of
+    // tiles nTPS+NS-TPS .. nTPS+NS-1 into them.
+    static_assert(NS >= 2 * TPS && NS - 2 * TPS <= 3, "ring size");
     TileIter<NT> it;
     it.init(a, h, i0, S, last_row / kTile);
-    int t[NS];                       // kt_n .. kt_{n+NS-1}
+    int t[NS];                       // tiles nTPS .. nTPS+NS-1 (-1 past the end)
     unsigned m[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -397,45 +442,52 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
         dma_tile<T, D, NW>(c, c.vbytes, kt, slot_addr + TILE_BYTES);
     };
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
+    for (int i = 0; i < NS - TPS; ++i)
         if (t[i] >= 0) issue(t[i], i);
-    // step n waits for kt_n; the loads of kt_{n+1} .. kt_{n+NS-2} may stay in flight
-    int inflight = (NS == 3 && t[1] >= 0) ? STEP_LOADS : 0;
 
-    // ---- main loop: one key tile per step ------------------------------------
+    // ---- main loop: TPS key tiles per step -------------------------------------
     for (int n = 0; t[0] >= 0; ++n) {
-        if (NS == 3 && inflight == STEP_LOADS) wait_vmcnt<STEP_LOADS>(); else __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                     // every wave's loads of kt_n landed; slot (n-1) mod NS is free
-        const int kt = t[0];
-        const bool act = active(c, kt, m[0]);
-        if (act) load_q(a, c, st, region_of_tile(c, kt));
-        if (t[NS - 1] >= 0) {
-            issue(t[NS - 1], n + NS - 1);
-            inflight = STEP_LOADS;
-        } else {
-            inflight = 0;
-        }
-        if (act) {
-            const char *cur = lds + (n % NS) * 2 * TILE_BYTES;
-            f32x16 s[2];
-            tile_scores<T, D>(c, st, cur, s);
-            if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
-            vec p[2][NUV];
-            float psum = tile_p<T>(s, p);
-            const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
-            if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
-                raise_ref<T, D>(st, s);
-                psum = tile_p<T>(s, p);
+        // tiles at window positions TPS .. NS-TPS-1 may stay in flight
+        int pending = 0;
+#pragma unroll
+        for (int i = TPS; i < NS - TPS; ++i) pending += t[i] >= 0;
+        wait_tiles<STEP_LOADS, NS - 2 * TPS>(pending);
+        __syncthreads();                     // step n's tiles landed; the slots of step n-1 are free
+        if (active(c, t[0], m[0])) load_q(a, c, st, region_of_tile(c, t[0]));
+#pragma unroll
+        for (int i = 0; i < TPS; ++i)
+            if (t[NS - TPS + i] >= 0) issue(t[NS - TPS + i], n * TPS + NS - TPS + i);
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            const int kt = t[i];
+            if (kt >= 0 && active(c, kt, m[i])) {
+                if (i > 0) load_q(a, c, st, region_of_tile(c, kt));
+                const char *cur = lds + ((n * TPS + i) % NS) * 2 * TILE_BYTES;
+                f32x16 s[2];
+                tile_scores<T, D>(c, st, cur, s);
+                if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
+                VFrags<T, D> vf;
+                load_v<T, D>(c, cur + TILE_BYTES, vf);
+                __builtin_amdgcn_sched_barrier(0);
+                vec p[2][NUV];
+                float psum = tile_p<T>(s, p);
+                const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
+                if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
+                    raise_ref<T, D>(st, s);
+                    psum = tile_p<T>(s, p);
+                }
+                st.l_run += psum;
+                __builtin_amdgcn_sched_barrier(0);
+                tile_pv<T, D>(st, vf, p);
             }
-            st.l_run += psum;
-            tile_pv<T, D>(c, st, cur + TILE_BYTES, p);
         }
 #pragma unroll
-        for (int i = 0; i < NS - 1; ++i) {
-            t[i] = t[i + 1];
-            m[i] = m[i + 1];
+        for (int i = 0; i < NS - TPS; ++i) {
+            t[i] = t[i + TPS];
+            m[i] = m[i + TPS];
         }
-        t[NS - 1] = t[NS - 1] >= 0 ? it.next(m[NS - 1]) : -1;
+#pragma unroll
+        for (int i = NS - TPS; i < NS; ++i) t[i] = t[i - 1] >= 0 ? it.next(m[i]) : -1;
     }
 
     // ---- epilogue -----------------------------------------------------------
@@ -458,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     }
 }
 
-template <typename T, int D, int NW, int NS>
+template <typename T, int D, int NW, int NS, int TPS>
 static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     constexpr int BM = kBlk * NW;
     AttnArgs a = a0;
@@ -472,7 +524,7 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     a.per_xcd = (int32_t)(per_stream * a.M * a.G);
     const int64_t grid = (int64_t)a.per_xcd * kXcds;
     const int lds_bytes = NS * 2 * (2 * kBlk * D * (int)sizeof(T));   // NS slots of [K tile | V tile]
-    auto kern = dca_attention_kernel<T, D, NW, NS>;
+    auto kern = dca_attention_kernel<T, D, NW, NS, TPS>;
     if (lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  lds_bytes);
@@ -505,10 +557,10 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
         a.list_stride = (int32_t)p.n_tiles;
     }
     if (p.dtype == DCA_BF16)
-        return p.D == 128 ? launch_attn_t<__bf16, 128, 8, 3>(p, a, stream)
-                          : launch_attn_t<__bf16, 64, 8, 3>(p, a, stream);
-    return p.D == 128 ? launch_attn_t<float, 128, 2, 2>(p, a, stream)
-                      : launch_attn_t<float, 64, 4, 3>(p, a, stream);
+        return p.D == 128 ? launch_attn_t<__bf16, 128, 8, 4, 2>(p, a, stream)
+                          : launch_attn_t<__bf16, 64, 8, 4, 2>(p, a, stream);
+    return p.D == 128 ? launch_attn_t<float, 128, 2, 2, 1>(p, a, stream)
+                      : launch_attn_t<float, 64, 4, 4, 2>(p, a, stream);
 }
 
 }  // namespace dca
