@@ -13,7 +13,8 @@ Prints ONE JSON line. `value` is whole-step TFLOP/s on the 1M-token Qwen2.5-14B
 layer shape (dense causal work 4 d Hq S(S+1)/2); `roofline` reports the
 attention kernel against the bf16 dense MFMA peak; `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload; `extra` holds the other
-measured workloads (128K dense and 1M vertical-slash).
+measured workloads (128K dense, 1M vertical-slash, and the 1M sequence as a
+chunked prefill in 32,768-row blocks).
 """
 
 from __future__ import annotations
@@ -168,6 +169,51 @@ def measure(name, steps, warmup, device):
     return w, res
 
 
+def measure_chunked(name, chunk, steps, warmup, device):
+    """Chunked prefill [mizuki, Chunked Prefill]: the whole sequence of the
+    workload as blocks of `chunk` rows, each one dca_prefill_chunk call on a
+    workspace that holds every key but only one block's query variants. The
+    blocks' q, k and v are resident in HBM before timing."""
+    w = workloads.get(name)
+    log(f"[bench] generating inputs for {name}, blocks of {chunk} rows")
+    q, k, v = synth.make_qkv(w, seed=0, device=device)
+    shape = api.shape_of(q, k)
+    blocks = []
+    for q0 in range(0, w.seq, chunk):
+        n = min(chunk, w.seq - q0)
+        blocks.append((q0, n, q[:, :, q0:q0 + n].contiguous(), k[:, :, q0:q0 + n].contiguous(),
+                       v[:, :, q0:q0 + n].contiguous()))
+    del q, k, v
+    nbytes = api.dca_chunk_workspace_size(w.seq, min(chunk, w.seq), w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, device)
+    outs = [torch.empty_like(b[2]) for b in blocks]
+
+    def run():
+        for (q0, n, qc, kc, vc), oc in zip(blocks, outs):
+            api.dca_prefill_chunk(qc, kc, vc, oc, None, q0, n, w.seq, w.chunk, w.window, w.rope_base,
+                                  w.yarn_scale, None, shape, ws, nbytes)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        run()
+        log(f"[bench] {name} in blocks of {chunk}: pass {i + 1}/{steps} enqueued")
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = {"workload": f"{name}_chunked{chunk}", "block_rows": chunk, "calls_per_step": len(blocks),
+           "ms_per_step": ms, "tflops": w.dense_flops() / (ms * 1e-3) / 1e12,
+           "workspace_bytes": nbytes, "whole_sequence_workspace_bytes": api.dca_workspace_size(
+               w.seq, w.chunk, w.window, shape)}
+    log(f"[bench] {json.dumps(res)}")
+    del blocks, outs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, n_rows=8, seed=0):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
     n_rows query rows spread over the sequence, every head. Reported in the
@@ -230,7 +276,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen14b_1m")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 128K and vertical-slash workloads")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 128K, vertical-slash and chunked-prefill workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -257,6 +304,7 @@ def main():
             if name != args.workload:
                 steps = 10 if name == "qwen7b_128k" else max(1, args.steps)
                 extra.append(measure(name, steps, 2 if name == "qwen7b_128k" else 1, dev)[1])
+        extra.append(measure_chunked("qwen14b_1m", 32768, 1, 1, dev))
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]

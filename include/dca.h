@@ -128,6 +128,36 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
                 const dca_vs_mask *mask, const dca_shape *shape,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Chunked prefill [mizuki, Chunked Prefill]: the sequence of seq tokens is
+ * prefilled a block of rows at a time, in order, on one workspace.
+ *
+ * dca_chunk_workspace_size: bytes of workspace for calls on this sequence
+ * with up to max_rows rows each (1 <= max_rows <= seq). The rotated keys and
+ * re-laid-out values of all seq positions stay in the workspace between
+ * calls; the query variants of one call come after them.
+ *
+ * dca_prefill_chunk: computes the query rows [q_offset, q_offset + n_rows)
+ * against the keys [0, q_offset + n_rows). q is [batch][n_q_heads][n_rows]
+ * [head_dim], k and v are [batch][n_kv_heads][n_rows][head_dim]: the rows and
+ * keys of this block only (device, read-only). out is [batch][n_q_heads]
+ * [n_rows][head_dim], lse [batch][n_q_heads][n_rows] float32 or NULL. The
+ * call rotates and stores this block's keys and values in the workspace, so
+ * the blocks before it (rows [0, q_offset)) must have been passed to earlier
+ * calls on the same workspace, with the same seq, C, W, rope_base,
+ * yarn_scale and shape (the keys are stored scaled by yarn_scale); calls on
+ * one workspace must not overlap in time. q_offset must be a multiple of 64
+ * (DCA_E_UNSUPPORTED) and the rows must lie inside [0, seq) (DCA_E_INVALID).
+ * The outputs are identical to the rows [q_offset, q_offset + n_rows) of one
+ * dca_prefill over the whole sequence. Other arguments and errors are as for
+ * dca_prefill. */
+int dca_chunk_workspace_size(int64_t seq, int64_t max_rows, int64_t C, int64_t W,
+                             const dca_shape *shape, const dca_vs_mask *mask, size_t *bytes);
+int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, float *lse,
+                      int64_t q_offset, int64_t n_rows, int64_t seq, int64_t C, int64_t W,
+                      double rope_base, float yarn_scale, const dca_vs_mask *mask,
+                      const dca_shape *shape, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* The three stages of dca_prefill, callable one at a time on the same
  * workspace (for per-stage timing and checks):
  *   dca_remap      -- the RoPE/DCA pre-pass: writes the cos/sin table, the

@@ -23,6 +23,7 @@ DCA_F32, DCA_BF16 = 0, 1
 EXPORTS = [
     "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
     "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
+    "dca_chunk_workspace_size", "dca_prefill_chunk",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
 ]
 
@@ -57,6 +58,9 @@ _SIGS = {
     "dca_remap": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float, _VP, _VP,
                                  ctypes.c_size_t, _VP]),
     "dca_vs_index": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_chunk_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
+    "dca_prefill_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
+                                         ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_debug_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "dca_debug_tile_regions": (ctypes.c_int, [_I64, _I64, _VP, _VP]),
@@ -174,6 +178,21 @@ def dca_attention(out, lse, seq, C, W, mask, shape, workspace, workspace_bytes, 
                                _ptr(workspace), workspace_bytes, _stream(stream)), "dca_attention")
 
 
+def dca_chunk_workspace_size(seq: int, max_rows: int, C: int, W: int, shape: dca_shape,
+                             mask: dca_vs_mask | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dca_chunk_workspace_size(seq, max_rows, C, W, ctypes.byref(shape), _ref(mask), ctypes.byref(n)),
+           "dca_chunk_workspace_size")
+    return n.value
+
+
+def dca_prefill_chunk(q, k, v, out, lse, q_offset, n_rows, seq, C, W, rope_base, yarn_scale, mask, shape,
+                      workspace, workspace_bytes, stream=None):
+    _check(lib().dca_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_offset, n_rows, seq, C, W,
+                                   rope_base, yarn_scale, _ref(mask), ctypes.byref(shape), _ptr(workspace),
+                                   workspace_bytes, _stream(stream)), "dca_prefill_chunk")
+
+
 def dca_debug_positions(seq, C, W, pq_intra, pq_succ, pq_inter, pk, stream=None):
     _check(lib().dca_debug_positions(seq, C, W, _ptr(pq_intra), _ptr(pq_succ), _ptr(pq_inter), _ptr(pk),
                                      _stream(stream)), "dca_debug_positions")
@@ -230,4 +249,33 @@ def prefill(q, k, v, C: int, W: int, rope_base: float = 1e7, yarn_scale: float =
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     dca_prefill(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
                 workspace.numel())
+    return (out, lse) if return_lse else out
+
+
+def prefill_chunked(q, k, v, C: int, W: int, chunk: int, rope_base: float = 1e7, yarn_scale: float = 1.0,
+                    vertical=None, slash=None, return_lse: bool = False, softmax_scale: float = 0.0):
+    """Chunked DCA prefill: the same result as prefill(), computed by
+    dca_prefill_chunk over blocks of `chunk` rows (a multiple of 64) on one
+    workspace sized for the whole sequence's keys and one block's queries."""
+    if chunk < 64 or chunk % 64 != 0:
+        raise ValueError("chunk must be a positive multiple of 64")
+    seq = q.shape[2]
+    shape = shape_of(q, k, softmax_scale)
+    mask = make_mask(vertical, slash)
+    nbytes = dca_chunk_workspace_size(seq, min(chunk, seq), C, W, shape, mask)
+    workspace = alloc_workspace(nbytes, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    for q0 in range(0, seq, chunk):
+        n = min(chunk, seq - q0)
+        qc = q[:, :, q0:q0 + n].contiguous()
+        kc = k[:, :, q0:q0 + n].contiguous()
+        vc = v[:, :, q0:q0 + n].contiguous()
+        oc = torch.empty_like(qc)
+        lc = torch.empty(qc.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+        dca_prefill_chunk(qc, kc, vc, oc, lc, q0, n, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
+                          workspace.numel())
+        out[:, :, q0:q0 + n] = oc
+        if return_lse:
+            lse[:, :, q0:q0 + n] = lc
     return (out, lse) if return_lse else out

@@ -49,9 +49,7 @@ Layout layout_for(const Problem &p) {
         return at;
     };
     L.table = take((size_t)p.n_pos * (size_t)(p.D / 2) * 8);
-    const size_t qbytes = (size_t)p.B * p.Hq * p.S_pad * p.D * p.esize;
     const size_t kvbytes = (size_t)p.B * p.Hkv * p.S_pad * p.D * p.esize;
-    for (int i = 0; i < 3; ++i) L.q[i] = take(qbytes);
     L.k = take(kvbytes);
     L.v = take(kvbytes);
     if (p.sparse) {
@@ -61,6 +59,8 @@ Layout layout_for(const Problem &p) {
         L.vs_dl = take((size_t)p.Hq * p.n_tiles * 4);
         L.vs_dl_n = take((size_t)p.Hq * 4);
     }
+    const size_t qbytes = (size_t)p.B * p.Hq * p.NQ_pad * p.D * p.esize;
+    for (int i = 0; i < 3; ++i) L.q[i] = take(qbytes);
     L.total = off;
     return L;
 }
@@ -96,6 +96,9 @@ static int make_problem(int64_t seq, int64_t C, int64_t W, const dca_shape *shap
     q.D = shape->head_dim;
     q.S = seq;
     q.S_pad = (seq + kSeqPad - 1) / kSeqPad * kSeqPad;
+    q.q0 = 0;
+    q.NQ = seq;
+    q.NQ_pad = q.S_pad;
     q.C = C;
     q.W = W;
     q.p_inter = C + W - 1;
@@ -120,6 +123,20 @@ static int make_problem(int64_t seq, int64_t C, int64_t W, const dca_shape *shap
         q.n_slash = mask->n_slash;
     }
     *p = q;
+    return DCA_OK;
+}
+
+// Restrict p to the query rows [q_offset, q_offset + n_rows) of its sequence.
+static int set_chunk(int64_t q_offset, int64_t n_rows, Problem *p) {
+    if (n_rows < 1) return fail(DCA_E_INVALID, "n_rows must be >= 1 (got %lld)", (long long)n_rows);
+    if (q_offset < 0 || q_offset > p->S - n_rows)
+        return fail(DCA_E_INVALID, "rows [%lld, %lld) are not inside the sequence of %lld tokens",
+                    (long long)q_offset, (long long)(q_offset + n_rows), (long long)p->S);
+    if (q_offset % kTile != 0)
+        return fail(DCA_E_UNSUPPORTED, "q_offset must be a multiple of %d (got %lld)", kTile, (long long)q_offset);
+    p->q0 = q_offset;
+    p->NQ = n_rows;
+    p->NQ_pad = (n_rows + kSeqPad - 1) / kSeqPad * kSeqPad;
     return DCA_OK;
 }
 
@@ -233,9 +250,9 @@ static int check_outputs(const Problem &p, const void *out, const float *lse, co
                          int n_inputs, const void *ws, size_t ws_bytes) {
     if (out == nullptr) return fail(DCA_E_INVALID, "out is NULL");
     if (misaligned(out, 16) || misaligned(lse, 4)) return fail(DCA_E_INVALID, "out must be 16-byte and lse 4-byte aligned");
-    const size_t obytes = (size_t)p.B * p.Hq * p.S * p.D * p.esize;
-    const size_t kvbytes = (size_t)p.B * p.Hkv * p.S * p.D * p.esize;
-    const size_t lbytes = lse ? (size_t)p.B * p.Hq * p.S * 4 : 0;
+    const size_t obytes = (size_t)p.B * p.Hq * p.NQ * p.D * p.esize;
+    const size_t kvbytes = (size_t)p.B * p.Hkv * p.NQ * p.D * p.esize;
+    const size_t lbytes = lse ? (size_t)p.B * p.Hq * p.NQ * 4 : 0;
     for (int i = 0; i < n_inputs; ++i) {
         const size_t ib = i == 0 ? obytes : kvbytes;   // q first, then k, v
         if (overlaps(out, obytes, inputs[i], ib)) return fail(DCA_E_INVALID, "out overlaps an input");
@@ -267,6 +284,46 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
     Layout L;
     int st = make_problem(seq, C, W, shape, mask, &p);
     if (st) return st;
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const void *inputs[3] = {q, k, v};
+    if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
+    if (p.sparse) {
+        const int err = launch_vs_index(p, *mask, workspace, L, stream);
+        if (err) return device_fail(err, "vertical-slash index launch");
+    }
+    const int err = launch_attention(p, out, lse, workspace, L, stream);
+    if (err) return device_fail(err, "attention launch");
+    return ok();
+}
+
+int dca_chunk_workspace_size(int64_t seq, int64_t max_rows, int64_t C, int64_t W, const dca_shape *shape,
+                             const dca_vs_mask *mask, size_t *bytes) {
+    if (bytes == nullptr) return fail(DCA_E_INVALID, "bytes is NULL");
+    Problem p;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if (max_rows < 1 || max_rows > seq)
+        return fail(DCA_E_INVALID, "max_rows must be in [1, seq] (got %lld)", (long long)max_rows);
+    if ((st = set_chunk(0, max_rows, &p))) return st;
+    *bytes = layout_for(p).total;
+    return ok();
+}
+
+int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, float *lse, int64_t q_offset,
+                      int64_t n_rows, int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale,
+                      const dca_vs_mask *mask, const dca_shape *shape, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if ((st = set_chunk(q_offset, n_rows, &p))) return st;
     if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
         return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");

@@ -41,8 +41,10 @@ struct AttnArgs {
     const void *vf;
     void *out;
     float *lse;
-    int64_t S, C;
-    int32_t Hq, Hkv, G, nblk;
+    int64_t S, C;                // S: end of the call's rows (= keys visible to the last row)
+    int64_t q0, NQ;              // the call's rows are [q0, q0 + NQ); out and lse hold NQ rows
+    int32_t Hq, Hkv, G;
+    int32_t nblk_q, nblk_kv;     // 32-row blocks per head in the query / key-value sections
     // work decode
     int32_t n_rt, KVH, s_split, M, per_xcd;
     // vertical-slash lists
@@ -392,7 +394,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
     const int S = (int)a.S;
-    const int i0 = rt * BM;
+    const int q0 = (int)a.q0;
+    const int i0 = q0 + rt * BM;
     const int last_row = (i0 + BM < S ? i0 + BM : S) - 1;
     WaveCtx c;
     c.lane = lane;
@@ -408,9 +411,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     c.tb_intra = cq * tiles_per_chunk;
     c.tb_succ = cq >= 1 ? c.tb_intra - tiles_per_chunk : 0;
     c.wave_qt = (kBlk * wave) / kTile;
-    c.qbase = (bh * a.nblk + c.r0 / kBlk) * (int64_t)BLK_ELEMS;
-    c.kbytes = (const char *)a.kf + bkv * a.nblk * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
-    c.vbytes = (const char *)a.vf + bkv * a.nblk * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
+    c.qbase = (bh * a.nblk_q + (c.r0 - q0) / kBlk) * (int64_t)BLK_ELEMS;
+    c.kbytes = (const char *)a.kf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
+    c.vbytes = (const char *)a.vf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
 
     WaveState<T, D> st;
     st.region = -1;
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     if (!c.active_rows || row >= S) return;
     const float l_tot = st.l_run + lane_swap32(st.l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T *orow = (T *)a.out + (bh * a.S + row) * D;
+    T *orow = (T *)a.out + (bh * a.NQ + (row - q0)) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
         }
     if (a.lse != nullptr && c.gsel == 0) {
         // natural log: (mref + log2 l) ln 2
-        a.lse[bh * a.S + row] = l_tot > 0.f ? (st.mref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        a.lse[bh * a.NQ + (row - q0)] = l_tot > 0.f ? (st.mref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
@@ -514,7 +517,7 @@ template <typename T, int D, int NW, int NS, int TPS>
 static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     constexpr int BM = kBlk * NW;
     AttnArgs a = a0;
-    a.n_rt = (int32_t)((p.S + BM - 1) / BM);
+    a.n_rt = (int32_t)((p.NQ + BM - 1) / BM);
     int gcd = 1;
     for (int d = 1; d <= kXcds; ++d)
         if (a.KVH % d == 0 && kXcds % d == 0) gcd = d;
@@ -541,12 +544,15 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
     a.vf = (const char *)ws + L.v;
     a.out = out;
     a.lse = lse;
-    a.S = p.S;
+    a.S = p.q0 + p.NQ;
+    a.q0 = p.q0;
+    a.NQ = p.NQ;
     a.C = p.C;
     a.Hq = (int32_t)p.Hq;
     a.Hkv = (int32_t)p.Hkv;
     a.G = (int32_t)p.G;
-    a.nblk = (int32_t)(p.S_pad / kBlk);
+    a.nblk_q = (int32_t)(p.NQ_pad / kBlk);
+    a.nblk_kv = (int32_t)(p.S_pad / kBlk);
     a.KVH = (int32_t)(p.B * p.Hkv);
     a.sparse = p.sparse ? 1 : 0;
     if (p.sparse) {
@@ -556,6 +562,10 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
         a.dl_n = (const int32_t *)((const char *)ws + L.vs_dl_n);
         a.list_stride = (int32_t)p.n_tiles;
     }
+    // Sparse: 128-row workgroups, two per CU. A workgroup visits the union of
+    // its query tiles' active key tiles, so fewer query tiles per workgroup
+    // leave fewer waves idle on each visited tile.
+    if (p.dtype == DCA_BF16 && p.sparse && p.D == 128) return launch_attn_t<__bf16, 128, 4, 2, 1>(p, a, stream);
     if (p.dtype == DCA_BF16)
         return p.D == 128 ? launch_attn_t<__bf16, 128, 8, 4, 2>(p, a, stream)
                           : launch_attn_t<__bf16, 64, 8, 4, 2>(p, a, stream);

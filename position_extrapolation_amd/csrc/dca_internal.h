@@ -42,9 +42,12 @@ struct RopeTheta {
     double theta[kMaxHalfDim];       // base^(-2m/d), m < d/2
 };
 
-// Validated problem description plus derived constants.
+// Validated problem description plus derived constants. A call computes the
+// query rows [q0, q0 + NQ) of a sequence of S tokens against the keys
+// [0, q0 + NQ); a whole-sequence prefill has q0 = 0 and NQ = S.
 struct Problem {
     int64_t B, Hq, Hkv, G, D, S, S_pad, C, W;
+    int64_t q0, NQ, NQ_pad;          // first row, rows, rows padded to 256
     int64_t p_inter;                 // C + W - 1
     int64_t n_pos;                   // C + W positions in the cos/sin table
     int64_t n_tiles;                 // ceil(S / 64)
@@ -55,14 +58,17 @@ struct Problem {
     int32_t n_vertical, n_slash;
 };
 
-// Byte offsets inside the workspace (each 256-byte aligned).
+// Byte offsets inside the workspace (each 256-byte aligned). Everything but
+// the query variants depends on the sequence alone, so one workspace serves
+// every chunk of a chunked prefill; the query variants come last and hold the
+// rows of one call.
 struct Layout {
     size_t table;                    // float2 [n_pos][D/2]
-    size_t q[3];                     // Q intra / succ / inter  [B*Hq][S_pad*D]
     size_t k;                        // rotated K               [B*Hkv][S_pad*D]
     size_t v;                        // V re-layout             [B*Hkv][S_pad*D]
     size_t vs_flags;                 // uint8 [2][Hq][n_tiles] (sparse only)
     size_t vs_vt, vs_vt_n, vs_dl, vs_dl_n;  // int32 lists and counts (sparse only)
+    size_t q[3];                     // Q intra / succ / inter  [B*Hq][NQ_pad*D]
     size_t total;
 };
 

@@ -47,8 +47,12 @@ int launch_rope_table(const Problem &p, double rope_base, void *ws, const Layout
 
 // ---------------------------------------------------------------------------
 // remap kernel
-// grid.x = S_pad / 32 row blocks; grid.y = B * (Hq + Hkv + Hkv): query heads,
-// then key heads (rotated), then value heads (re-laid out).
+// The inputs hold the n rows [q0, q0 + n) of the sequence (q0 = 0, n = S for a
+// whole-sequence call). grid.x = ceil(n / 256) * 8 row blocks of 32; grid.y =
+// B * (Hq + Hkv + Hkv): query heads, then key heads (rotated), then value
+// heads (re-laid out). Query variants are written at the call's own row
+// blocks; keys and values at their blocks in the sequence, up to the end of
+// the last 64-key tile the call's rows can see (rows past n as zeros).
 // ---------------------------------------------------------------------------
 struct RemapArgs {
     const void *q, *k, *v;
@@ -56,8 +60,10 @@ struct RemapArgs {
     void *kf, *vf;
     const float2 *table;
     float k_scale;               // multiplies the rotated keys
-    int64_t S, C, W;
-    int32_t Hq, Hkv, nblk;
+    int64_t n, q0, C, W;         // input rows per head, their first sequence index
+    int32_t Hq, Hkv;
+    int32_t nblk_q, nblk_kv;     // 32-row blocks per head in the query / key-value sections
+    int32_t kv_blk_end;          // key-value blocks [q0 / 32, kv_blk_end) are written
 };
 
 template <typename T, int D>
@@ -74,17 +80,19 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
     const int per_b = a.Hq + 2 * a.Hkv;
     const int b = y / per_b;
     const int hh = y % per_b;
+    const int64_t kv_blk = a.q0 / kBlk + blk;     // the block's place in the key-value sections
+    if (hh >= a.Hq && kv_blk >= a.kv_blk_end) return;
 
     if (hh >= a.Hq + a.Hkv) {
         // ---- V re-layout through LDS -------------------------------------
         const int h = hh - a.Hq - a.Hkv;
         const int64_t bh = (int64_t)b * a.Hkv + h;
         __shared__ T tile[kBlk][D + 2 * E];
-        const T *src = (const T *)a.v + (bh * a.S + blk * kBlk) * D;
+        const T *src = (const T *)a.v + (bh * a.n + blk * kBlk) * D;
         for (int c = threadIdx.x; c < kBlk * D / E; c += blockDim.x) {
             const int r = c / (D / E), col = (c % (D / E)) * E;
             typename F::vec val;
-            if (blk * kBlk + r < a.S) {
+            if (blk * kBlk + r < a.n) {
                 val = *(const typename F::vec *)(src + (int64_t)r * D + col);
             } else {
                 val = F::zero();
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
         __syncthreads();
         // fragment (db, u, lane): element e = V[2E u + 8 (e/4) + 4 g + e%4][32 db + x]
         constexpr int NUV = kBlk / (2 * E);
-        T *dst = (T *)a.vf + (bh * a.nblk + blk) * BLK_ELEMS;
+        T *dst = (T *)a.vf + (bh * a.nblk_kv + kv_blk) * BLK_ELEMS;
         for (int f = threadIdx.x; f < (D / 32) * NUV * 64; f += blockDim.x) {
             const int lane = f % 64, u = (f / 64) % NUV, db = f / (64 * NUV);
             const int x = lane % 32, g = lane / 32;
@@ -115,17 +123,18 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
     const int h = is_q ? hh : hh - a.Hq;
     const int H = is_q ? a.Hq : a.Hkv;
     const int64_t bh = (int64_t)b * H + h;
-    const T *src = (const T *)(is_q ? a.q : a.k) + bh * a.S * D;
+    const T *src = (const T *)(is_q ? a.q : a.k) + bh * a.n * D;
     const int nvar = is_q ? 3 : 1;
 
     for (int item = threadIdx.x; item < kBlk * NP; item += blockDim.x) {
         const int ri = item / NP, c = item % NP;
-        const int64_t i = blk * kBlk + ri;
-        const bool valid = i < a.S;
+        const int64_t il = blk * kBlk + ri;       // input row
+        const int64_t i = a.q0 + il;              // sequence index
+        const bool valid = il < a.n;
         typename F::vec x1 = F::zero(), x2 = F::zero();
         if (valid) {
-            x1 = *(const typename F::vec *)(src + i * D + c * E);
-            x2 = *(const typename F::vec *)(src + i * D + HALF + c * E);
+            x1 = *(const typename F::vec *)(src + il * D + c * E);
+            x2 = *(const typename F::vec *)(src + il * D + HALF + c * E);
         }
         float f1[E], f2[E];
 #pragma unroll
@@ -154,7 +163,8 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
                     F::set(y2, e, F::from_float((f2[e] * t.x + f1[e] * t.y) * sc));
                 }
             }
-            T *dst = (T *)(is_q ? a.qf[var] : a.kf) + (bh * a.nblk + blk) * BLK_ELEMS;
+            T *dst = is_q ? (T *)a.qf[var] + (bh * a.nblk_q + blk) * BLK_ELEMS
+                          : (T *)a.kf + (bh * a.nblk_kv + kv_blk) * BLK_ELEMS;
             *(typename F::vec *)(dst + off1) = y1;
             *(typename F::vec *)(dst + off2) = y2;
         }
@@ -174,13 +184,16 @@ static int launch_remap_t(const Problem &p, const void *q, const void *k, const 
     a.kf = (char *)ws + L.k;
     a.vf = (char *)ws + L.v;
     a.table = (const float2 *)((char *)ws + L.table);
-    a.S = p.S;
+    a.n = p.NQ;
+    a.q0 = p.q0;
     a.C = p.C;
     a.W = p.W;
     a.Hq = (int32_t)p.Hq;
     a.Hkv = (int32_t)p.Hkv;
-    a.nblk = (int32_t)(p.S_pad / kBlk);
-    dim3 grid((unsigned)(p.S_pad / kBlk), (unsigned)(p.B * (p.Hq + 2 * p.Hkv)));
+    a.nblk_q = (int32_t)(p.NQ_pad / kBlk);
+    a.nblk_kv = (int32_t)(p.S_pad / kBlk);
+    a.kv_blk_end = (int32_t)((p.q0 + p.NQ + kTile - 1) / kTile * (kTile / kBlk));
+    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (p.Hq + 2 * p.Hkv)));
     hipLaunchKernelGGL((remap_kernel<T, D>), grid, dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
@@ -266,7 +279,7 @@ static int launch_unpack_t(const Problem &p, const void *ws, const Layout &L, in
     const int threads = 256;
     hipLaunchKernelGGL((debug_unpack_kernel<T, D>), dim3((unsigned)((n + threads - 1) / threads)),
                        dim3(threads), 0, (hipStream_t)stream, (const T *)((const char *)ws + base),
-                       (T *)dst, p.S, p.S_pad / kBlk, n, which == 4 ? 1 : 0);
+                       (T *)dst, p.S, (which < 3 ? p.NQ_pad : p.S_pad) / kBlk, n, which == 4 ? 1 : 0);
     return (int)hipGetLastError();
 }
 

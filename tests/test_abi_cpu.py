@@ -108,6 +108,49 @@ def test_valid_call_without_gpu_reports_device_error():
     assert "HIP error" in api.dca_last_error()
 
 
+def test_chunk_workspace_size():
+    sh = api.make_shape(1, 28, 4, 128, torch.bfloat16)
+    S, C, W = 32768, 8192, 1024
+    whole = api.dca_workspace_size(S, C, W, sh)
+    assert api.dca_chunk_workspace_size(S, S, C, W, sh) == whole
+    small = api.dca_chunk_workspace_size(S, 4096, C, W, sh)
+    # three query variants of 4096 rows instead of 32768
+    assert whole - small == 3 * 28 * (S - 4096) * 128 * 2
+    for bad in (0, S + 1):
+        with pytest.raises(api.DcaError):
+            api.dca_chunk_workspace_size(S, bad, C, W, sh)
+
+
+def _call_chunk(**over):
+    sh = api.make_shape(1, 2, 1, 64, torch.float32)
+    args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, q_offset=512, n_rows=256,
+                seq=2048, C=512, W=128, base=1e7, yarn=1.0, ws=0x50000000, ws_bytes=1 << 30)
+    args.update(over)
+    return api.lib().dca_prefill_chunk(args["q"], args["k"], args["v"], args["out"], args["lse"], args["q_offset"],
+                                       args["n_rows"], args["seq"], args["C"], args["W"], args["base"],
+                                       args["yarn"], None, ctypes.byref(sh), args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q_offset=100), api.DCA_E_UNSUPPORTED),          # not a multiple of 64
+    (dict(q_offset=-64), api.DCA_E_INVALID),
+    (dict(n_rows=0), api.DCA_E_INVALID),
+    (dict(q_offset=1920, n_rows=256), api.DCA_E_INVALID),  # past the sequence
+    (dict(ws_bytes=1 << 20), api.DCA_E_WORKSPACE),
+    (dict(out=0x10000000 + 4096), api.DCA_E_INVALID),     # out overlaps q
+    (dict(k=None), api.DCA_E_INVALID),
+])
+def test_chunk_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_chunk(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_valid_chunk_call_without_gpu_reports_device_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_chunk() == api.DCA_E_DEVICE
+
+
 def test_status_strings():
     for s in range(5):
         assert api.dca_status_str(s).startswith("DCA_")

@@ -360,3 +360,76 @@ def test_vs_parity(S, C, W, nv, ns):
     say(f"  max abs err out={err:.3e} lse={lerr:.3e}; dense-vs-sparse distance {dd:.3e}")
     assert err <= TOL["bf16"] and lerr <= 2e-2
     assert err <= 0.1 * dd
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill: rows [q0, q0 + n) against keys [0, q0 + n), one workspace
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,S,C,W,chunk", [
+    ("bf16", 4, 2, 128, 8292, 2048, 512, 1536),   # blocks not a multiple of 256, ragged last block
+    ("bf16", 3, 1, 64, 1000, 128, 128, 64),       # 64-row blocks
+    ("f32", 2, 1, 64, 2048, 512, 128, 320),       # fp32, blocks straddle chunk boundaries
+    ("bf16", 2, 1, 128, 4096, 4096, 100, 4096),   # one block = the whole sequence
+])
+def test_chunked_equals_whole_prefill(dtype, Hq, Hkv, D, S, C, W, chunk):
+    say(f"[chunked] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W} chunk={chunk}")
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=21, device=DEV)
+    full, full_lse = _run(q, k, v, w)
+    out, lse = api.prefill_chunked(q, k, v, C, W, chunk, w.rope_base, w.yarn_scale, return_lse=True)
+    torch.cuda.synchronize()
+    # every wave sees the same rows, keys and tile order either way
+    assert torch.equal(out, full)
+    assert torch.equal(lse, full_lse)
+    rows = synth.sample_rows(S, C, W, 96, seed=3)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    err = _err(out[:, :, rows_t], ref)
+    say(f"  bit-identical to the whole-sequence call; max abs err vs oracle {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_chunked_vertical_slash_equals_whole():
+    say("[chunked vs] S=8192 C=2048 W=256 chunk=2048 nv=80 ns=120")
+    w = _wl("qwen14b_1m_vs", seq=8192, chunk=2048, window=256, n_vertical=80, n_slash=120, n_q_heads=4,
+            n_kv_heads=2)
+    q, k, v = synth.make_qkv(w, seed=4, device=DEV)
+    vert, slash = _vs_case(w, seed=4)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    full, full_lse = _run(q, k, v, w, vertical=vd, slash=sd)
+    out, lse = api.prefill_chunked(q, k, v, w.chunk, w.window, 2048, w.rope_base, w.yarn_scale, vertical=vd,
+                                   slash=sd, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full)
+    assert torch.equal(lse, full_lse)
+
+
+def test_chunk_reads_only_earlier_blocks():
+    """A block's output does not depend on keys past its last row: the same
+    block computed with the later rows of q, k and v replaced by noise."""
+    say("[chunk causality] bf16 S=4096 C=1024 W=128, block [1024, 2048)")
+    w = workloads.Workload("t", 1, 2, 1, 128, 4096, 1024, 128, "bf16", 0.5, True)
+    q, k, v = synth.make_qkv(w, seed=5, device=DEV)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_chunk_workspace_size(4096, 1024, w.chunk, w.window, shape)
+    outs = []
+    for noise in (False, True):
+        ws = api.alloc_workspace(nbytes, DEV)
+        k2, v2 = k.clone(), v.clone()
+        if noise:
+            k2[:, :, 2048:] = torch.randn_like(k2[:, :, 2048:].float()).to(k2.dtype) * 4
+            v2[:, :, 2048:] = torch.randn_like(v2[:, :, 2048:].float()).to(v2.dtype) * 4
+            # a later block written first must not leak into an earlier one
+            o = torch.empty_like(q[:, :, 2048:3072])
+            api.dca_prefill_chunk(q[:, :, 2048:3072].contiguous(), k2[:, :, 2048:3072].contiguous(),
+                                  v2[:, :, 2048:3072].contiguous(), o, None, 2048, 1024, 4096, w.chunk, w.window,
+                                  w.rope_base, w.yarn_scale, None, shape, ws, nbytes)
+        for q0 in (0, 1024):
+            o = torch.empty_like(q[:, :, q0:q0 + 1024])
+            api.dca_prefill_chunk(q[:, :, q0:q0 + 1024].contiguous(), k2[:, :, q0:q0 + 1024].contiguous(),
+                                  v2[:, :, q0:q0 + 1024].contiguous(), o, None, q0, 1024, 4096, w.chunk, w.window,
+                                  w.rope_base, w.yarn_scale, None, shape, ws, nbytes)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1])

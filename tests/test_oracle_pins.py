@@ -274,6 +274,29 @@ def test_sampled_rows_equal_full_rows():
     assert torch.allclose(lp, lf[:, :, rows], rtol=0, atol=1e-13)
 
 
+def test_block_rows_depend_only_on_earlier_keys():
+    """[mizuki, Chunked Prefill]: a block of rows [q0, q0 + n) prefilled
+    against the keys [0, q0 + n) alone gives the rows of the whole-sequence
+    result; later keys, whatever they hold, change nothing (causality)."""
+    S, C, W = 240, 32, 8
+    q = _rand((1, 2, S, 16), 90)
+    k = _rand((1, 1, S, 16), 91)
+    v = _rand((1, 1, S, 16), 92)
+    full, lf = O.dca_prefill_rows(q, torch.arange(S), k, v, C, W, 1e7, 1.2)
+    for q0, n in [(0, 64), (64, 96), (160, 80)]:
+        rows = torch.arange(q0, q0 + n)
+        kp, vp = k[:, :, :q0 + n].clone(), v[:, :, :q0 + n].clone()
+        blk, lb = O.dca_prefill_rows(q[:, :, rows], rows, kp, vp, C, W, 1e7, 1.2)
+        assert torch.allclose(blk, full[:, :, rows], rtol=0, atol=1e-14)
+        assert torch.allclose(lb, lf[:, :, rows], rtol=0, atol=1e-13)
+        # the same rows with the later keys replaced by noise
+        kn, vn = k.clone(), v.clone()
+        kn[:, :, q0 + n:] = _rand(kn[:, :, q0 + n:].shape, 93, 5.0)
+        vn[:, :, q0 + n:] = _rand(vn[:, :, q0 + n:].shape, 94, 5.0)
+        bn, _ = O.dca_prefill_rows(q[:, :, rows], rows, kn, vn, C, W, 1e7, 1.2)
+        assert torch.allclose(bn, full[:, :, rows], rtol=0, atol=1e-14)
+
+
 def test_planted_needle_dominates_output():
     """Plant a key whose rotated copy is a multiple of the row's rotated query
     in the pair's region: the output of that row is then almost the needle's
