@@ -214,6 +214,48 @@ def measure_chunked(name, chunk, steps, warmup, device):
     return res
 
 
+def measure_decode(name, steps, device):
+    """DCA decode of the last `steps` tokens of the workload's sequence, one
+    dca_decode call each, against the key/value cache of everything before
+    them (filled by the remap pre-pass). Bound by HBM: each call reads the
+    cache once, (pos + 1) keys and values per KV head."""
+    w = workloads.get(name)
+    log(f"[bench] generating inputs for {name} decode")
+    q, k, v = synth.make_qkv(w, seed=0, device=device)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_workspace_size(w.seq, w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, device)
+    api.dca_remap(q, k, v, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, shape, ws, nbytes)
+    first = w.seq - steps
+    toks = [(pos, q[:, :, pos].contiguous(), k[:, :, pos].contiguous(), v[:, :, pos].contiguous())
+            for pos in range(first, w.seq)]
+    del q, k, v
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=toks[0][1].dtype, device=device)
+
+    def run():
+        for pos, qt, kt, vt in toks:
+            api.dca_decode(qt, kt, vt, out, None, pos, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale,
+                           shape, ws, nbytes)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    esize = 2 if w.dtype == "bf16" else 4
+    cache_bytes = np.mean([(pos + 1) * w.batch * w.n_kv_heads * w.head_dim * 2 * esize for pos, *_ in toks])
+    res = {"workload": f"{name}_decode", "tokens": steps, "context": w.seq, "ms_per_token": ms,
+           "cache_bytes_per_token": cache_bytes, "hbm_gbs": cache_bytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": cache_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    log(f"[bench] {json.dumps(res)}")
+    del toks, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, n_rows=8, seed=0):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
     n_rows query rows spread over the sequence, every head. Reported in the
@@ -305,6 +347,7 @@ def main():
                 steps = 10 if name == "qwen7b_128k" else max(1, args.steps)
                 extra.append(measure(name, steps, 2 if name == "qwen7b_128k" else 1, dev)[1])
         extra.append(measure_chunked("qwen14b_1m", 32768, 1, 1, dev))
+        extra.append(measure_decode("qwen14b_1m", 64, dev))
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]

@@ -158,6 +158,28 @@ int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, fl
                       const dca_shape *shape, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* DCA decode of one new token per sequence [mizuki, Intra-/Successive-/
+ * Inter-Chunk Attention, DCA + YaRN]: the token at sequence index pos (the
+ * same for every batch entry) attends to the keys [0, pos] with the DCA
+ * position map of row pos; the result equals row pos of a prefill over the
+ * first pos + 1 tokens. q is [batch][n_q_heads][head_dim], k and v are
+ * [batch][n_kv_heads][head_dim]: the new token's query, key and value
+ * (device, read-only). The call first stores the rotated key and the value at
+ * index pos of the workspace's key/value cache, so the keys [0, pos) must
+ * have been stored by earlier dca_prefill, dca_prefill_chunk or dca_decode
+ * calls on the same workspace with the same seq, C, W, rope_base, yarn_scale
+ * and shape; seq is the capacity the workspace was sized for
+ * (dca_workspace_size or dca_chunk_workspace_size with any max_rows) and
+ * 0 <= pos < seq (DCA_E_INVALID). n_q_heads / n_kv_heads must be <= 32
+ * (DCA_E_UNSUPPORTED); the vertical-slash mask is a prefill feature and is
+ * not taken here. out: device [batch][n_q_heads][head_dim]; lse: device
+ * float32 [batch][n_q_heads] or NULL. The scratch of the split-key reduction
+ * lives in the workspace's query section. Errors are as for dca_prefill. */
+int dca_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+               int64_t pos, int64_t seq, int64_t C, int64_t W, double rope_base,
+               float yarn_scale, const dca_shape *shape, void *workspace,
+               size_t workspace_bytes, void *stream);
+
 /* The three stages of dca_prefill, callable one at a time on the same
  * workspace (for per-stage timing and checks):
  *   dca_remap      -- the RoPE/DCA pre-pass: writes the cos/sin table, the

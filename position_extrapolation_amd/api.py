@@ -23,7 +23,7 @@ DCA_F32, DCA_BF16 = 0, 1
 EXPORTS = [
     "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
     "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
-    "dca_chunk_workspace_size", "dca_prefill_chunk",
+    "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
 ]
 
@@ -61,6 +61,8 @@ _SIGS = {
     "dca_chunk_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
     "dca_prefill_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
                                          ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float,
+                                  _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_debug_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "dca_debug_tile_regions": (ctypes.c_int, [_I64, _I64, _VP, _VP]),
@@ -191,6 +193,12 @@ def dca_prefill_chunk(q, k, v, out, lse, q_offset, n_rows, seq, C, W, rope_base,
     _check(lib().dca_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_offset, n_rows, seq, C, W,
                                    rope_base, yarn_scale, _ref(mask), ctypes.byref(shape), _ptr(workspace),
                                    workspace_bytes, _stream(stream)), "dca_prefill_chunk")
+
+
+def dca_decode(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
+               stream=None):
+    _check(lib().dca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pos, seq, C, W, rope_base, yarn_scale,
+                            ctypes.byref(shape), _ptr(workspace), workspace_bytes, _stream(stream)), "dca_decode")
 
 
 def dca_debug_positions(seq, C, W, pq_intra, pq_succ, pq_inter, pk, stream=None):

@@ -342,6 +342,36 @@ int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, fl
     return ok();
 }
 
+int dca_decode(const void *q, const void *k, const void *v, void *out, float *lse, int64_t pos, int64_t seq,
+               int64_t C, int64_t W, double rope_base, float yarn_scale, const dca_shape *shape, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, nullptr, &p);
+    if (st) return st;
+    if (pos < 0 || pos >= seq)
+        return fail(DCA_E_INVALID, "pos must be in [0, seq) (got %lld, seq %lld)", (long long)pos, (long long)seq);
+    if (p.G > kBlk)
+        return fail(DCA_E_UNSUPPORTED, "decode needs n_q_heads / n_kv_heads <= %d (got %lld)", kBlk, (long long)p.G);
+    p.q0 = pos;
+    p.NQ = 1;
+    p.NQ_pad = kSeqPad;
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    if (decode_scratch_bytes(p) > L.total - L.q[0])
+        return fail(DCA_E_WORKSPACE, "query section too small for the decode scratch");
+    const void *inputs[3] = {q, k, v};
+    if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    const float k_scale = yarn_scale * p.softmax_scale * 1.4426950408889634f;
+    const int err = launch_decode(p, q, k, v, out, lse, rope_base, k_scale, workspace, L, stream);
+    if (err) return device_fail(err, "decode launch");
+    return ok();
+}
+
 int dca_debug_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
                         int32_t *pq_inter, int32_t *pk, void *stream) {
     if (seq < 1 || seq >= ((int64_t)1 << 31)) return fail(DCA_E_INVALID, "seq out of range");

@@ -96,6 +96,10 @@ int launch_remap(const Problem &p, const void *q, const void *k, const void *v, 
                  const Layout &L, void *stream);
 int launch_vs_index(const Problem &p, const dca_vs_mask &m, void *ws, const Layout &L, void *stream);
 int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream);
+// decode of the token at index p.q0 (p.NQ = 1); scratch lives in the query section
+int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
+                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream);
+size_t decode_scratch_bytes(const Problem &p);
 int launch_debug_positions(int64_t S, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
                            int32_t *pq_inter, int32_t *pk, void *stream);
 int launch_debug_tile_regions(int64_t S, int64_t C, uint8_t *out, void *stream);

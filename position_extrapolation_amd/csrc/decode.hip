@@ -1,0 +1,315 @@
+// DCA decode for gfx950: one new token per sequence against the key/value
+// cache that a prefill left in the workspace.
+//
+// The new token sits at sequence index pos. Its query takes the three DCA
+// positions of row pos -- intra pos mod C, successive min(C + pos mod C,
+// C + W - 1), inter C + W - 1 [mizuki, Intra-/Successive-/Inter-Chunk
+// Attention] -- and attends to the keys [0, pos], each key at j mod C, with
+// the variant picked by the chunk distance of the key tile; the logits carry
+// the YaRN temperature through the pre-scaled keys [mizuki, DCA + YaRN]. The
+// result equals row pos of a prefill over the first pos + 1 tokens.
+//
+// Three launches:
+//   decode_prep_kernel    rotates the new key (at pos mod C, scaled) and
+//                         writes it and the new value into the cache at index
+//                         pos (zero-filling the rest of a fresh 64-key tile),
+//                         and rotates the new query three ways;
+//   decode_attn_kernel    split-K flash decoding: one wave per (KV group,
+//                         split of the key tiles). The wave's 32 score
+//                         columns are the query heads of the KV group, so
+//                         every K and V fragment read from HBM feeds all G
+//                         heads through the same 64-key tile step as the
+//                         prefill; it writes a partial (max, sum, O) per head;
+//   decode_combine_kernel merges the splits per head.
+// The attention launch is bound by HBM: it reads the cache once.
+#include <hip/hip_runtime.h>
+
+#include "dca_internal.h"
+#include "frag.h"
+#include "tile_math.h"
+
+namespace dca {
+
+constexpr int kMaxSplits = 256;
+
+struct DecodeArgs {
+    const void *q, *k, *v;       // new token: q [B][Hq][D], k and v [B][Hkv][D]
+    void *kf, *vf;               // cache sections of the workspace
+    void *qv;                    // rotated query variants [B][Hq][3][D]
+    float *part;                 // partials [B][Hq][kMaxSplits][D + 2]: O, max (log2 units), sum
+    void *out;                   // [B][Hq][D]
+    float *lse;                  // [B][Hq] or null
+    RopeTheta th;
+    float k_scale;               // yarn * softmax scale * log2 e
+    int64_t pos, C, W;
+    int32_t Hq, Hkv, G, nblk_kv;
+    int32_t n_split, tiles_per_split;
+};
+
+// cos and sin of p * theta_m, the same float64 formula as the prefill table
+__device__ __forceinline__ float2 rope_cs(const DecodeArgs &a, int64_t p, int m) {
+    const double ang = (double)p * a.th.theta[m];
+    return make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// ---------------------------------------------------------------------------
+// prep: grid B * (Hq + Hkv + Hkv) blocks of 128 threads
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(128) void decode_prep_kernel(DecodeArgs a) {
+    using F = Frag<T>;
+    constexpr int E = F::E;
+    constexpr int HALF = D / 2;
+    constexpr int BLK_ELEMS = kBlk * D;
+    constexpr int NUV = kBlk / (2 * E);
+    const int per_b = a.Hq + 2 * a.Hkv;
+    const int b = blockIdx.x / per_b;
+    const int hh = blockIdx.x % per_b;
+    const int t = threadIdx.x;
+
+    if (hh < a.Hq) {
+        // query: three rotated variants, rounded to the operand type
+        if (t >= HALF) return;
+        const int64_t bh = (int64_t)b * a.Hq + hh;
+        const T *x = (const T *)a.q + bh * D;
+        const float x1 = (float)x[t], x2 = (float)x[t + HALF];
+        T *dst = (T *)a.qv + bh * 3 * D;
+        for (int var = 0; var < 3; ++var) {
+            const int64_t p = var == 0 ? pos_intra(a.pos, a.C)
+                                       : (var == 1 ? pos_succ(a.pos, a.C, a.W) : pos_inter(a.C, a.W));
+            const float2 cs = rope_cs(a, p, t);
+            dst[var * D + t] = F::from_float(x1 * cs.x - x2 * cs.y);
+            dst[var * D + t + HALF] = F::from_float(x2 * cs.x + x1 * cs.y);
+        }
+        return;
+    }
+    const bool is_k = hh < a.Hq + a.Hkv;
+    const int h = is_k ? hh - a.Hq : hh - a.Hq - a.Hkv;
+    const int64_t bh = (int64_t)b * a.Hkv + h;
+    // rows pos .. row_end - 1 are written: the new token, then zeros to the
+    // end of its 64-key tile when the token opens that tile
+    const int64_t row_end = (a.pos % kTile == 0) ? a.pos + kTile : a.pos + 1;
+    if (is_k) {
+        const T *x = (const T *)a.k + bh * D;
+        for (int64_t r = a.pos; r < row_end; ++r) {
+            T *blk = (T *)a.kf + (bh * a.nblk_kv + r / kBlk) * BLK_ELEMS;
+            const int ri = (int)(r % kBlk);
+            for (int d = t; d < D; d += blockDim.x) {
+                float y = 0.f;
+                if (r == a.pos) {
+                    const int m = d % HALF;
+                    const float x1 = (float)x[m], x2 = (float)x[m + HALF];
+                    const float2 cs = rope_cs(a, pos_key(a.pos, a.C), m);
+                    y = d < HALF ? (x1 * cs.x - x2 * cs.y) * a.k_scale : (x2 * cs.x + x1 * cs.y) * a.k_scale;
+                }
+                // fragment slot of element d of row ri (operand order of dca_internal.h)
+                const int c = d / E, e = d % E;
+                blk[((int64_t)(c / 2) * 64 + (c % 2) * 32 + ri) * E + e] = F::from_float(y);
+            }
+        }
+    } else {
+        const T *x = (const T *)a.v + bh * D;
+        for (int64_t r = a.pos; r < row_end; ++r) {
+            T *blk = (T *)a.vf + (bh * a.nblk_kv + r / kBlk) * BLK_ELEMS;
+            const int ri = (int)(r % kBlk);
+            // key ri = key(u, g, e) = 2E u + 8 (e / 4) + 4 g + e % 4
+            const int u = ri / (2 * E), rem = ri % (2 * E);
+            const int g = (rem % 8) / 4, e = 4 * (rem / 8) + rem % 4;
+            for (int d = t; d < D; d += blockDim.x) {
+                const T val = r == a.pos ? x[d] : F::from_float(0.f);
+                const int db = d / 32, lane = 32 * g + d % 32;
+                blk[(((int64_t)db * NUV + u) * 64 + lane) * E + e] = val;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// attention: grid (n_split, B * Hkv) waves
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void decode_attn_kernel(DecodeArgs a) {
+    using F = Frag<T>;
+    using vec = typename F::vec;
+    constexpr int E = F::E;
+    constexpr int NU = D / (2 * E);
+    constexpr int NUV = kBlk / (2 * E);
+    constexpr int NDB = D / 32;
+    constexpr int BLK_ELEMS = kBlk * D;
+    constexpr int TILE_BYTES = 2 * BLK_ELEMS * (int)sizeof(T);
+
+    const int split = blockIdx.x;
+    const int bkv_i = blockIdx.y;
+    const int b = bkv_i / a.Hkv;
+    const int kvh = bkv_i % a.Hkv;
+    const int64_t bkv = (int64_t)b * a.Hkv + kvh;
+    const int lane = threadIdx.x;
+    const int x = lane % 32, g = lane / 32;
+    const bool col_ok = x < a.G;                       // column x = query head kvh * G + x
+    const int64_t bh = (int64_t)b * a.Hq + (int64_t)kvh * a.G + (col_ok ? x : 0);
+
+    const int n_tiles = (int)(a.pos / kTile) + 1;
+    const int kt0 = split * a.tiles_per_split;
+    const int kt1 = min(kt0 + a.tiles_per_split, n_tiles);
+    const int cq = (int)(a.pos / a.C);
+    const char *kbase = (const char *)a.kf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
+    const char *vbase = (const char *)a.vf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
+
+    WaveState<T, D> st;
+    st.region = -1;
+    st.first = true;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
+    st.mref = 0.f;
+    st.l_run = 0.f;
+
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int region = region_of(cq, (int64_t)kt * kTile / a.C);
+        if (region != st.region) {
+            const vec *qs = (const vec *)((const T *)a.qv + (bh * 3 + region) * D);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) st.qfrag[u] = col_ok ? qs[2 * u + g] : F::zero();
+            st.region = region;
+        }
+        const char *kl = kbase + (int64_t)kt * TILE_BYTES;
+        // the tile's V fragments are requested together with its K fragments
+        VFrags<T, D> vf;
+        load_v<T, D>(lane, vbase + (int64_t)kt * TILE_BYTES, vf);
+        f32x16 s[2];
+        tile_scores<T, D, false>(lane, st, kl, s);
+        const int lim = (int)(a.pos - (int64_t)kt * kTile);   // key offset k is kept iff k <= lim
+        if (lim < kTile - 1) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (kBlk * kb + 8 * (v / 4) + 4 * g + (v % 4) > lim) s[kb][v] = -INFINITY;
+        }
+        vec p[2][NUV];
+        float psum = tile_p<T>(s, p);
+        const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
+        if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
+            raise_ref<T, D>(st, s);
+            psum = tile_p<T>(s, p);
+        }
+        st.l_run += psum;
+        tile_pv<T, D>(st, vf, p);
+    }
+
+    if (!col_ok) return;
+    float *part = a.part + (bh * kMaxSplits + split) * (D + 2);
+    const float l_tot = st.l_run + lane_swap32(st.l_run);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[32 * db + 8 * (v / 4) + 4 * g + (v % 4)] = st.oacc[db][v];
+    if (g == 0) {
+        part[D] = st.first ? -INFINITY : st.mref;
+        part[D + 1] = st.first ? 0.f : l_tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine: grid B * Hq blocks of 256 threads (one per split slot)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kMaxSplits) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int NT = kMaxSplits;
+    constexpr int RPT = NT / D;                  // threads sharing one output element
+    __shared__ float wgt[NT];                    // 2^(m_s - M), 0 for empty splits
+    __shared__ float red[NT];
+    const int64_t bh = blockIdx.x;
+    const int t = threadIdx.x;
+    const float *part = a.part + bh * kMaxSplits * (D + 2);
+    const bool live = t < a.n_split && part[t * (D + 2) + D + 1] > 0.f;
+    const float m = live ? part[t * (D + 2) + D] : -INFINITY;
+    // M = max over the live splits
+    red[t] = m;
+    __syncthreads();
+    for (int w = NT / 2; w > 0; w /= 2) {
+        if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+        __syncthreads();
+    }
+    const float mx = red[0];
+    __syncthreads();
+    const float wt = live ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
+    wgt[t] = wt;
+    red[t] = live ? wt * part[t * (D + 2) + D + 1] : 0.f;
+    __syncthreads();
+    for (int w = NT / 2; w > 0; w /= 2) {
+        if (t < w) red[t] += red[t + w];
+        __syncthreads();
+    }
+    const float den = red[0];
+    __syncthreads();
+    // O[d] = sum_s w_s O_s[d] / den: thread t sums every RPT-th split of element t % D
+    const int d = t % D, r = t / D;
+    float num = 0.f;
+    for (int s = r; s < a.n_split; s += RPT) num += wgt[s] * part[s * (D + 2) + d];
+    red[t] = num;
+    __syncthreads();
+    if (r == 0) {
+        for (int i = 1; i < RPT; ++i) num += red[i * D + d];
+        ((T *)a.out)[bh * D + d] = Frag<T>::from_float(den > 0.f ? num / den : 0.f);
+        if (a.lse != nullptr && d == 0)
+            a.lse[bh] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+template <typename T, int D>
+static int launch_decode_t(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
+                           double rope_base, float k_scale, void *ws, const Layout &L, void *stream) {
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kf = (char *)ws + L.k;
+    a.vf = (char *)ws + L.v;
+    a.qv = (char *)ws + L.q[0];
+    const size_t qv_bytes = ((size_t)p.B * p.Hq * 3 * D * sizeof(T) + 255) & ~(size_t)255;
+    a.part = (float *)((char *)ws + L.q[0] + qv_bytes);
+    a.out = out;
+    a.lse = lse;
+    for (int m = 0; m < D / 2; ++m) a.th.theta[m] = pow(rope_base, -2.0 * m / (double)D);
+    a.k_scale = k_scale;
+    a.pos = p.q0;
+    a.C = p.C;
+    a.W = p.W;
+    a.Hq = (int32_t)p.Hq;
+    a.Hkv = (int32_t)p.Hkv;
+    a.G = (int32_t)p.G;
+    a.nblk_kv = (int32_t)(p.S_pad / kBlk);
+    // about 2048 waves in flight over the cache, at most kMaxSplits per KV group
+    const int64_t n_tiles = p.q0 / kTile + 1;
+    const int64_t groups = p.B * p.Hkv;
+    int64_t want = (2048 + groups - 1) / groups;
+    want = want < kMaxSplits ? want : kMaxSplits;
+    want = want < n_tiles ? want : n_tiles;
+    a.tiles_per_split = (int32_t)((n_tiles + want - 1) / want);
+    a.n_split = (int32_t)((n_tiles + a.tiles_per_split - 1) / a.tiles_per_split);
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL((decode_prep_kernel<T, D>), dim3((unsigned)(p.B * (p.Hq + 2 * p.Hkv))), dim3(128), 0, s, a);
+    int err = (int)hipGetLastError();
+    if (err) return err;
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3((unsigned)a.n_split, (unsigned)groups), dim3(64), 0, s, a);
+    err = (int)hipGetLastError();
+    if (err) return err;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(p.B * p.Hq)), dim3(kMaxSplits), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+size_t decode_scratch_bytes(const Problem &p) {
+    const size_t qv = ((size_t)p.B * p.Hq * 3 * p.D * p.esize + 255) & ~(size_t)255;
+    return qv + (size_t)p.B * p.Hq * kMaxSplits * (p.D + 2) * sizeof(float);
+}
+
+int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
+                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream) {
+    if (p.dtype == DCA_BF16)
+        return p.D == 128 ? launch_decode_t<__bf16, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream)
+                          : launch_decode_t<__bf16, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream);
+    return p.D == 128 ? launch_decode_t<float, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream)
+                      : launch_decode_t<float, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream);
+}
+
+}  // namespace dca

@@ -151,6 +151,36 @@ def test_valid_chunk_call_without_gpu_reports_device_error():
     assert _call_chunk() == api.DCA_E_DEVICE
 
 
+def _call_decode(**over):
+    sh = over.pop("shape", api.make_shape(1, 4, 2, 64, torch.float32))
+    args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, pos=700, seq=2048, C=512,
+                W=128, base=1e7, yarn=1.0, ws=0x50000000, ws_bytes=1 << 30)
+    args.update(over)
+    return api.lib().dca_decode(args["q"], args["k"], args["v"], args["out"], args["lse"], args["pos"], args["seq"],
+                                args["C"], args["W"], args["base"], args["yarn"], ctypes.byref(sh), args["ws"],
+                                args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(pos=-1), api.DCA_E_INVALID),
+    (dict(pos=2048), api.DCA_E_INVALID),
+    (dict(v=None), api.DCA_E_INVALID),
+    (dict(ws_bytes=1 << 16), api.DCA_E_WORKSPACE),
+    (dict(shape=api.make_shape(1, 66, 2, 64, torch.float32)), api.DCA_E_UNSUPPORTED),   # 33 heads per group
+    (dict(out=0x30000000), api.DCA_E_INVALID),            # out aliases v
+    (dict(yarn=-1.0), api.DCA_E_INVALID),
+])
+def test_decode_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_decode(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_valid_decode_call_without_gpu_reports_device_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_decode() == api.DCA_E_DEVICE
+
+
 def test_status_strings():
     for s in range(5):
         assert api.dca_status_str(s).startswith("DCA_")

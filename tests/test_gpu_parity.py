@@ -433,3 +433,76 @@ def test_chunk_reads_only_earlier_blocks():
         torch.cuda.synchronize()
         outs.append(o)
     assert torch.equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------------------
+# decode: one new token at index pos against the cache a prefill left behind
+# ---------------------------------------------------------------------------
+
+def _decode_run(q, k, v, w, prompt, steps):
+    """Prefill rows [0, prompt) as one block (when prompt > 0), then decode the
+    tokens prompt .. prompt + steps - 1 one at a time on the same workspace."""
+    shape = api.shape_of(q, k)
+    S = w.seq
+    nbytes = api.dca_chunk_workspace_size(S, max(prompt, 1), w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    if prompt > 0:
+        o = torch.empty_like(q[:, :, :prompt])
+        api.dca_prefill_chunk(q[:, :, :prompt].contiguous(), k[:, :, :prompt].contiguous(),
+                              v[:, :, :prompt].contiguous(), o, None, 0, prompt, S, w.chunk, w.window, w.rope_base,
+                              w.yarn_scale, None, shape, ws, nbytes)
+    outs, lses = [], []
+    for pos in range(prompt, prompt + steps):
+        o = torch.empty_like(q[:, :, pos])
+        l = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+        api.dca_decode(q[:, :, pos].contiguous(), k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), o, l, pos, S,
+                       w.chunk, w.window, w.rope_base, w.yarn_scale, shape, ws, nbytes)
+        outs.append(o)
+        lses.append(l)
+    torch.cuda.synchronize()
+    return torch.stack(outs, 2), torch.stack(lses, 2)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,S,C,W,prompt", [
+    ("bf16", 8, 2, 128, 2200, 512, 64, 2040),    # decode crosses a 64-key tile (2048) and keeps going
+    ("bf16", 5, 1, 128, 1100, 1024, 128, 1020),  # crosses the chunk boundary at 1024: intra -> new chunk
+    ("f32", 4, 2, 64, 700, 128, 32, 600),        # fp32, d = 64, G = 2
+    ("bf16", 7, 1, 64, 40, 64, 8, 0),            # no prompt: decode from pos 0 on a fresh workspace
+])
+def test_decode_matches_oracle(dtype, Hq, Hkv, D, S, C, W, prompt):
+    steps = min(S - prompt, 40)
+    say(f"[decode] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W} prompt={prompt} steps={steps}")
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=31, device=DEV)
+    out, lse = _decode_run(q, k, v, w, prompt, steps)
+    rows = np.arange(prompt, prompt + steps)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL[dtype]
+    assert lerr <= (1e-4 if dtype == "f32" else 2e-2)
+    if dtype == "bf16":
+        g = out.double().cpu()
+        assert ((g - ref).abs() <= ref.abs() * 2.0 ** -8 + 2e-3).all()
+
+
+def test_decode_long_context():
+    """Decode at a ~100K-token context (7B shape): the oracle on every decoded
+    row, the discrimination guard against wrong position maps, and agreement
+    with the prefill of the same rows."""
+    # rows just past the start of the fourth 32K chunk: row offset < W, where
+    # the successive-chunk position differs from the inter-chunk one
+    prompt, steps = 3 * 32768 + 100, 6
+    w = _wl("qwen7b_128k", seq=prompt + steps)
+    say(f"[decode ~100K] prompt={prompt} steps={steps}")
+    q, k, v = synth.make_qkv(w, seed=2, device=DEV)
+    out, lse = _decode_run(q, k, v, w, prompt, steps)
+    rows = np.arange(prompt, prompt + steps)
+    ref, _ = _oracle(q, k, v, rows, w)
+    err = _err(out, ref)
+    _discrimination(q, k, v, rows, w, ref, out)
+    pre, _ = _run(q, k, v, w)
+    dp = (out.float() - pre[:, :, rows.tolist()].float()).abs().max().item()
+    say(f"  max abs err {err:.3e}; decode vs prefill rows {dp:.3e}")
+    assert err <= TOL["bf16"]
+    assert dp <= TOL["bf16"]
