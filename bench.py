@@ -13,8 +13,9 @@ Prints ONE JSON line. `value` is whole-step TFLOP/s on the 1M-token Qwen2.5-14B
 layer shape (dense causal work 4 d Hq S(S+1)/2); `roofline` reports the
 attention kernel against the bf16 dense MFMA peak; `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload; `extra` holds the other
-measured workloads (128K dense, 1M vertical-slash, and the 1M sequence as a
-chunked prefill in 32,768-row blocks).
+measured workloads: 128K dense, 1M vertical-slash, the 1M sequence as a
+chunked prefill in 32,768-row blocks, decode at a 1M context, and the 1M path
+with the query rotation fused into the attention kernel.
 """
 
 from __future__ import annotations
@@ -214,6 +215,33 @@ def measure_chunked(name, chunk, steps, warmup, device):
     return res
 
 
+def measure_fused(name, device):
+    """The whole path with the query rotation fused into the attention kernel
+    (dca_prefill_fused): the pre-pass writes keys and values only."""
+    w = workloads.get(name)
+    log(f"[bench] generating inputs for {name}, fused query rotation")
+    q, k, v = synth.make_qkv(w, seed=0, device=device)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_fused_workspace_size(w.seq, w.chunk, w.window, shape)
+    ws = api.alloc_workspace(nbytes, device)
+    out = torch.empty_like(q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    api.dca_prefill_fused(q, k, v, out, None, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, None, shape,
+                          ws, nbytes)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    res = {"workload": f"{name}_fused_rotation", "ms_per_step": ms, "tflops": w.dense_flops() / (ms * 1e-3) / 1e12,
+           "workspace_bytes": nbytes,
+           "materialized_workspace_bytes": api.dca_workspace_size(w.seq, w.chunk, w.window, shape)}
+    log(f"[bench] {json.dumps(res)}")
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_decode(name, steps, device):
     """DCA decode of the last `steps` tokens of the workload's sequence, one
     dca_decode call each, against the key/value cache of everything before
@@ -348,6 +376,7 @@ def main():
                 extra.append(measure(name, steps, 2 if name == "qwen7b_128k" else 1, dev)[1])
         extra.append(measure_chunked("qwen14b_1m", 32768, 1, 1, dev))
         extra.append(measure_decode("qwen14b_1m", 64, dev))
+        extra.append(measure_fused("qwen14b_1m", dev))
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]

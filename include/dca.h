@@ -158,6 +158,24 @@ int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, fl
                       const dca_shape *shape, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* The whole path with the query rotation fused into the attention kernel
+ * [mizuki, Inter-Chunk Attention: only position indices change]: the pre-pass
+ * rotates and stores only the keys (and re-lays out the values); each wave
+ * reads its rows of q and turns them to the region's query position when it
+ * enters a region (three times per row block at most), with the same cos/sin
+ * table entries and the same arithmetic as the pre-pass, so out and lse are
+ * identical to dca_prefill's. The workspace (dca_fused_workspace_size) holds
+ * no query variants: 3 n_q_heads / (3 n_q_heads + 2 n_kv_heads) of the
+ * dca_prefill workspace less. q must stay unchanged until the call's work on
+ * the stream has finished. Arguments, layouts and errors are as for
+ * dca_prefill. */
+int dca_fused_workspace_size(int64_t seq, int64_t C, int64_t W, const dca_shape *shape,
+                             const dca_vs_mask *mask, size_t *bytes);
+int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, float *lse,
+                      int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale,
+                      const dca_vs_mask *mask, const dca_shape *shape,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* DCA decode of one new token per sequence [mizuki, Intra-/Successive-/
  * Inter-Chunk Attention, DCA + YaRN]: the token at sequence index pos (the
  * same for every batch entry) attends to the keys [0, pos] with the DCA

@@ -23,7 +23,8 @@ DCA_F32, DCA_BF16 = 0, 1
 EXPORTS = [
     "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
     "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
-    "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode",
+    "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode", "dca_fused_workspace_size",
+    "dca_prefill_fused",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
 ]
 
@@ -60,6 +61,9 @@ _SIGS = {
     "dca_vs_index": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_chunk_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
     "dca_prefill_chunk": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, ctypes.c_double,
+                                         ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_fused_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
+    "dca_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double,
                                          ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float,
                                   _VP, _VP, ctypes.c_size_t, _VP]),
@@ -195,6 +199,20 @@ def dca_prefill_chunk(q, k, v, out, lse, q_offset, n_rows, seq, C, W, rope_base,
                                    workspace_bytes, _stream(stream)), "dca_prefill_chunk")
 
 
+def dca_fused_workspace_size(seq: int, C: int, W: int, shape: dca_shape, mask: dca_vs_mask | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dca_fused_workspace_size(seq, C, W, ctypes.byref(shape), _ref(mask), ctypes.byref(n)),
+           "dca_fused_workspace_size")
+    return n.value
+
+
+def dca_prefill_fused(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
+                      workspace_bytes, stream=None):
+    _check(lib().dca_prefill_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), seq, C, W, rope_base,
+                                   yarn_scale, _ref(mask), ctypes.byref(shape), _ptr(workspace), workspace_bytes,
+                                   _stream(stream)), "dca_prefill_fused")
+
+
 def dca_decode(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
                stream=None):
     _check(lib().dca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pos, seq, C, W, rope_base, yarn_scale,
@@ -239,24 +257,26 @@ def yarn_logit_scale(seq: int, C: int) -> float:
 
 def prefill(q, k, v, C: int, W: int, rope_base: float = 1e7, yarn_scale: float = 1.0,
             vertical=None, slash=None, return_lse: bool = False, softmax_scale: float = 0.0,
-            workspace: torch.Tensor | None = None):
+            workspace: torch.Tensor | None = None, fused: bool = False):
     """DCA prefill on torch device tensors q [B, Hq, S, d], k and v [B, Hkv, S, d]
     (contiguous, one dtype); optional vertical [Hq, nv] / slash [Hq, ns] int32
     device tensors. Returns out (and lse) allocated with torch; the call is
-    enqueued on the current stream."""
+    enqueued on the current stream. fused=True rotates the queries inside the
+    attention kernel (dca_prefill_fused; smaller workspace, same results)."""
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k and v must be contiguous")
     seq = q.shape[2]
     shape = shape_of(q, k, softmax_scale)
     mask = make_mask(vertical, slash)
-    nbytes = dca_workspace_size(seq, C, W, shape, mask)
+    size = dca_fused_workspace_size if fused else dca_workspace_size
+    nbytes = size(seq, C, W, shape, mask)
     if workspace is None or workspace.numel() < nbytes:
         workspace = alloc_workspace(nbytes, q.device)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    dca_prefill(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace,
-                workspace.numel())
+    run = dca_prefill_fused if fused else dca_prefill
+    run(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask, shape, workspace, workspace.numel())
     return (out, lse) if return_lse else out
 
 

@@ -59,7 +59,7 @@ Layout layout_for(const Problem &p) {
         L.vs_dl = take((size_t)p.Hq * p.n_tiles * 4);
         L.vs_dl_n = take((size_t)p.Hq * 4);
     }
-    const size_t qbytes = (size_t)p.B * p.Hq * p.NQ_pad * p.D * p.esize;
+    const size_t qbytes = p.fused ? 0 : (size_t)p.B * p.Hq * p.NQ_pad * p.D * p.esize;
     for (int i = 0; i < 3; ++i) L.q[i] = take(qbytes);
     L.total = off;
     return L;
@@ -338,6 +338,43 @@ int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, fl
         if (err) return device_fail(err, "vertical-slash index launch");
     }
     const int err = launch_attention(p, out, lse, workspace, L, stream);
+    if (err) return device_fail(err, "attention launch");
+    return ok();
+}
+
+int dca_fused_workspace_size(int64_t seq, int64_t C, int64_t W, const dca_shape *shape, const dca_vs_mask *mask,
+                             size_t *bytes) {
+    if (bytes == nullptr) return fail(DCA_E_INVALID, "bytes is NULL");
+    Problem p;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    p.fused = true;
+    *bytes = layout_for(p).total;
+    return ok();
+}
+
+int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, float *lse, int64_t seq, int64_t C,
+                      int64_t W, double rope_base, float yarn_scale, const dca_vs_mask *mask,
+                      const dca_shape *shape, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    Layout L;
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    p.fused = true;
+    if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const void *inputs[3] = {q, k, v};
+    if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = do_remap(p, nullptr, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
+    if (p.sparse) {
+        const int err = launch_vs_index(p, *mask, workspace, L, stream);
+        if (err) return device_fail(err, "vertical-slash index launch");
+    }
+    const int err = launch_attention(p, out, lse, workspace, L, stream, q);
     if (err) return device_fail(err, "attention launch");
     return ok();
 }

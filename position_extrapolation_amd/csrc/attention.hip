@@ -38,11 +38,13 @@ namespace dca {
 
 struct AttnArgs {
     const void *qf[3];
+    const void *q_nat;           // fused rotation: the call's queries [B][Hq][NQ][D], rotated here
+    const float2 *table;         // fused rotation: cos/sin table [C + W][D/2]
     const void *kf;
     const void *vf;
     void *out;
     float *lse;
-    int64_t S, C;                // S: end of the call's rows (= keys visible to the last row)
+    int64_t S, C, W;             // S: end of the call's rows (= keys visible to the last row)
     int64_t q0, NQ;              // the call's rows are [q0, q0 + NQ); out and lse hold NQ rows
     int32_t Hq, Hkv, G;
     int32_t nblk_q, nblk_kv;     // 32-row blocks per head in the query / key-value sections
@@ -133,6 +135,7 @@ struct TileIter {
 struct WaveCtx {
     int lane, x, gsel, wave, r0, tb_succ, tb_intra, wave_qt;
     bool active_rows;
+    int64_t bh;                  // batch * n_q_heads + head
     int64_t qbase;               // element offset of this wave's 32-row block in a Q variant
     const char *kbytes, *vbytes; // this KV head's fragment-ordered K and V
 };
@@ -200,20 +203,48 @@ __device__ __forceinline__ void mask_diag(const WaveCtx &c, int j0, f32x16 (&s)[
             if (kBlk * kb + 8 * (v / 4) + (v % 4) > lim) s[kb][v] = -INFINITY;
 }
 
-template <typename T, int D>
+// The query fragments of the wave's rows for a region: read from the
+// rotated variant the pre-pass wrote, or (FUSED) read from the caller's
+// queries and turned here, with the same table entries and arithmetic as the
+// pre-pass, so both give the same bits. In a lane, fragment u and u + NU/2
+// hold the two halves (m, m + d/2) of the same rotation pairs.
+template <typename T, int D, bool FUSED>
 __device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, WaveState<T, D> &st, int region) {
-    using vec = typename Frag<T>::vec;
+    using F = Frag<T>;
+    using vec = typename F::vec;
+    constexpr int E = F::E;
+    constexpr int NU = WaveState<T, D>::NU;
     if (region == st.region) return;
-    const vec *qs = (const vec *)a.qf[region] + c.qbase / Frag<T>::E;
+    if constexpr (FUSED) {
+        const int row = c.r0 + c.x;
+        const bool valid = row < (int)a.S;
+        const T *src = (const T *)a.q_nat + ((c.bh * a.NQ) + (row - a.q0)) * D + E * c.gsel;
 #pragma unroll
-    for (int u = 0; u < WaveState<T, D>::NU; ++u) st.qfrag[u] = qs[u * 64 + c.lane];
+        for (int u = 0; u < NU; ++u) st.qfrag[u] = valid ? *(const vec *)(src + 2 * E * u) : F::zero();
+        const int64_t p = region == 0 ? pos_intra(row, a.C) : (region == 1 ? pos_succ(row, a.C, a.W) : pos_inter(a.C, a.W));
+        const float2 *tab = a.table + p * (D / 2) + E * c.gsel;
+#pragma unroll
+        for (int u = 0; u < NU / 2; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float2 cs = tab[2 * E * u + e];
+                const float2 r = rope_pair((float)F::get(st.qfrag[u], e), (float)F::get(st.qfrag[u + NU / 2], e),
+                                           cs.x, cs.y);
+                F::set(st.qfrag[u], e, F::from_float(r.x));
+                F::set(st.qfrag[u + NU / 2], e, F::from_float(r.y));
+            }
+    } else {
+        const vec *qs = (const vec *)a.qf[region] + c.qbase / E;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) st.qfrag[u] = qs[u * 64 + c.lane];
+    }
     st.region = region;
     // land them here (twice per row block at most): no compiler-counted load
     // is then outstanding while tile loads are in flight
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <typename T, int D, int NW, int NS, int TPS>
+template <typename T, int D, int NW, int NS, int TPS, bool FUSED>
 // second bound: at least two waves per SIMD (256 registers per wave)
 __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     using F = Frag<T>;
@@ -271,6 +302,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     c.tb_intra = cq * tiles_per_chunk;
     c.tb_succ = cq >= 1 ? c.tb_intra - tiles_per_chunk : 0;
     c.wave_qt = (kBlk * wave) / kTile;
+    c.bh = bh;
     c.qbase = (bh * a.nblk_q + (c.r0 - q0) / kBlk) * (int64_t)BLK_ELEMS;
     c.kbytes = (const char *)a.kf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
     c.vbytes = (const char *)a.vf + bkv * a.nblk_kv * (int64_t)BLK_ELEMS * (int64_t)sizeof(T);
@@ -316,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
         for (int i = TPS; i < NS - TPS; ++i) pending += t[i] >= 0;
         wait_tiles<STEP_LOADS, NS - 2 * TPS>(pending);
         __syncthreads();                     // step n's tiles landed; the slots of step n-1 are free
-        if (active(c, t[0], m[0])) load_q(a, c, st, region_of_tile(c, t[0]));
+        if (active(c, t[0], m[0])) load_q<T, D, FUSED>(a, c, st, region_of_tile(c, t[0]));
 #pragma unroll
         for (int i = 0; i < TPS; ++i)
             if (t[NS - TPS + i] >= 0) issue(t[NS - TPS + i], n * TPS + NS - TPS + i);
@@ -324,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
         for (int i = 0; i < TPS; ++i) {
             const int kt = t[i];
             if (kt >= 0 && active(c, kt, m[i])) {
-                if (i > 0) load_q(a, c, st, region_of_tile(c, kt));
+                if (i > 0) load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
                 const char *cur = lds + ((n * TPS + i) % NS) * 2 * TILE_BYTES;
                 f32x16 s[2];
                 tile_scores<T, D, true>(c.lane, st, cur, s);
@@ -387,7 +419,8 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     a.per_xcd = (int32_t)(per_stream * a.M * a.G);
     const int64_t grid = (int64_t)a.per_xcd * kXcds;
     const int lds_bytes = NS * 2 * (2 * kBlk * D * (int)sizeof(T));   // NS slots of [K tile | V tile]
-    auto kern = dca_attention_kernel<T, D, NW, NS, TPS>;
+    auto kern = a.q_nat != nullptr ? dca_attention_kernel<T, D, NW, NS, TPS, true>
+                                   : dca_attention_kernel<T, D, NW, NS, TPS, false>;
     if (lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  lds_bytes);
@@ -397,8 +430,12 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     return (int)hipGetLastError();
 }
 
-int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream) {
+int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream,
+                     const void *q_nat) {
     AttnArgs a{};
+    a.q_nat = q_nat;
+    a.table = (const float2 *)((const char *)ws + L.table);
+    a.W = p.W;
     for (int i = 0; i < 3; ++i) a.qf[i] = (const char *)ws + L.q[i];
     a.kf = (const char *)ws + L.k;
     a.vf = (const char *)ws + L.v;

@@ -55,6 +55,7 @@ struct Problem {
     int esize;                       // bytes per element
     float softmax_scale;
     bool sparse;
+    bool fused;                      // queries rotated inside the attention kernel: no query section
     int32_t n_vertical, n_slash;
 };
 
@@ -89,13 +90,23 @@ __host__ __device__ inline int region_of(int64_t cq, int64_t ck) {
     return d >= 2 ? 2 : (int)d;
 }
 
+// Half-split RoPE turn of the pair (x1, x2) = (x[m], x[m + d/2]) by the
+// angle with cosine c and sine s, in fp32: (x1 c - x2 s, x2 c + x1 s), each
+// with one explicit fused multiply-add, so that every kernel that rotates a
+// vector produces the same bits.
+__device__ inline float2 rope_pair(float x1, float x2, float c, float s) {
+    return make_float2(fmaf(x1, c, -(x2 * s)), fmaf(x2, c, x1 * s));
+}
+
 // Launchers (return hipError_t as int; 0 = success).
 int launch_rope_table(const Problem &p, double rope_base, void *ws, const Layout &L, void *stream);
 // k_scale multiplies the rotated keys (yarn * softmax scale * log2 e)
 int launch_remap(const Problem &p, const void *q, const void *k, const void *v, float k_scale, void *ws,
                  const Layout &L, void *stream);
 int launch_vs_index(const Problem &p, const dca_vs_mask &m, void *ws, const Layout &L, void *stream);
-int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream);
+// q_nat != null: fused rotation, the kernel turns the caller's queries itself
+int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream,
+                     const void *q_nat = nullptr);
 // decode of the token at index p.q0 (p.NQ = 1); scratch lives in the query section
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
                   double rope_base, float k_scale, void *ws, const Layout &L, void *stream);

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(128) void decode_prep_kernel(DecodeArgs a) {
             const int64_t p = var == 0 ? pos_intra(a.pos, a.C)
                                        : (var == 1 ? pos_succ(a.pos, a.C, a.W) : pos_inter(a.C, a.W));
             const float2 cs = rope_cs(a, p, t);
-            dst[var * D + t] = F::from_float(x1 * cs.x - x2 * cs.y);
-            dst[var * D + t + HALF] = F::from_float(x2 * cs.x + x1 * cs.y);
+            const float2 r = rope_pair(x1, x2, cs.x, cs.y);
+            dst[var * D + t] = F::from_float(r.x);
+            dst[var * D + t + HALF] = F::from_float(r.y);
         }
         return;
     }
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(128) void decode_prep_kernel(DecodeArgs a) {
                     const int m = d % HALF;
                     const float x1 = (float)x[m], x2 = (float)x[m + HALF];
                     const float2 cs = rope_cs(a, pos_key(a.pos, a.C), m);
-                    y = d < HALF ? (x1 * cs.x - x2 * cs.y) * a.k_scale : (x2 * cs.x + x1 * cs.y) * a.k_scale;
+                    const float2 rr = rope_pair(x1, x2, cs.x, cs.y);
+                    y = (d < HALF ? rr.x : rr.y) * a.k_scale;
                 }
                 // fragment slot of element d of row ri (operand order of dca_internal.h)
                 const int c = d / E, e = d % E;

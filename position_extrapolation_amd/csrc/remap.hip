@@ -159,8 +159,9 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float2 t = cs[e];
-                    F::set(y1, e, F::from_float((f1[e] * t.x - f2[e] * t.y) * sc));
-                    F::set(y2, e, F::from_float((f2[e] * t.x + f1[e] * t.y) * sc));
+                    const float2 r = rope_pair(f1[e], f2[e], t.x, t.y);
+                    F::set(y1, e, F::from_float(r.x * sc));
+                    F::set(y2, e, F::from_float(r.y * sc));
                 }
             }
             T *dst = is_q ? (T *)a.qf[var] + (bh * a.nblk_q + blk) * BLK_ELEMS
@@ -188,12 +189,12 @@ static int launch_remap_t(const Problem &p, const void *q, const void *k, const 
     a.q0 = p.q0;
     a.C = p.C;
     a.W = p.W;
-    a.Hq = (int32_t)p.Hq;
+    a.Hq = p.fused ? 0 : (int32_t)p.Hq;          // fused rotation: keys and values only
     a.Hkv = (int32_t)p.Hkv;
     a.nblk_q = (int32_t)(p.NQ_pad / kBlk);
     a.nblk_kv = (int32_t)(p.S_pad / kBlk);
     a.kv_blk_end = (int32_t)((p.q0 + p.NQ + kTile - 1) / kTile * (kTile / kBlk));
-    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (p.Hq + 2 * p.Hkv)));
+    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (a.Hq + 2 * p.Hkv)));
     hipLaunchKernelGGL((remap_kernel<T, D>), grid, dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }

@@ -121,6 +121,19 @@ def test_chunk_workspace_size():
             api.dca_chunk_workspace_size(S, bad, C, W, sh)
 
 
+def test_fused_workspace_size():
+    sh = api.make_shape(1, 28, 4, 128, torch.bfloat16)
+    S, C, W = 32768, 8192, 1024
+    whole = api.dca_workspace_size(S, C, W, sh)
+    fused = api.dca_fused_workspace_size(S, C, W, sh)
+    # no query variants: three query-sized sections less
+    assert whole - fused == 3 * 28 * S * 128 * 2
+    L = api.lib()
+    bad = L.dca_prefill_fused(0x10000000, 0x20000000, 0x30000000, 0x40000000, None, S, C, W, 1e7, 1.0, None,
+                              ctypes.byref(sh), 0x50000000, fused - 256, None)
+    assert bad == api.DCA_E_WORKSPACE
+
+
 def _call_chunk(**over):
     sh = api.make_shape(1, 2, 1, 64, torch.float32)
     args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, q_offset=512, n_rows=256,

@@ -506,3 +506,44 @@ def test_decode_long_context():
     say(f"  max abs err {err:.3e}; decode vs prefill rows {dp:.3e}")
     assert err <= TOL["bf16"]
     assert dp <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# fused query rotation: identical to the path with materialized variants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,S,C,W", [
+    ("bf16", 4, 2, 128, 3000, 1024, 256),   # ragged tail, three chunks
+    ("bf16", 3, 1, 64, 777, 128, 128),      # W = C, d = 64
+    ("f32", 2, 1, 64, 2048, 512, 128),
+    ("f32", 4, 1, 128, 515, 128, 32),
+])
+def test_fused_rotation_equals_materialized(dtype, Hq, Hkv, D, S, C, W):
+    say(f"[fused] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W}")
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=41, device=DEV)
+    ref_out, ref_lse = _run(q, k, v, w)
+    out, lse = api.prefill(q, k, v, C, W, w.rope_base, w.yarn_scale, return_lse=True, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    assert torch.equal(lse, ref_lse)
+    rows = synth.sample_rows(S, C, W, 64, seed=5)
+    ref, _ = _oracle(q, k, v, rows, w)
+    err = _err(out[:, :, torch.as_tensor(rows, device=DEV)], ref)
+    say(f"  bit-identical to the materialized path; max abs err vs oracle {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_fused_rotation_vertical_slash():
+    say("[fused vs] S=8192 C=2048 W=256 nv=80 ns=120")
+    w = _wl("qwen14b_1m_vs", seq=8192, chunk=2048, window=256, n_vertical=80, n_slash=120, n_q_heads=4,
+            n_kv_heads=2)
+    q, k, v = synth.make_qkv(w, seed=6, device=DEV)
+    vert, slash = _vs_case(w, seed=6)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    ref_out, ref_lse = _run(q, k, v, w, vertical=vd, slash=sd)
+    out, lse = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, vertical=vd, slash=sd,
+                           return_lse=True, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    assert torch.equal(lse, ref_lse)
