@@ -37,6 +37,14 @@ choice, listed again in the design notes):
                                                                [mizuki, 稀疏注意力 + 核优化]
   * causal, self included, positions start at 0; query head h reads KV head
     h // (Hq / Hkv).
+  * online vertical-slash selection (the pages only say that key tokens are
+    chosen from the attention map's vertical-slash pattern with continuous
+    relative positions restored): the last n query rows attend with RoPE at
+    their true indices (and the same logit scale as the attention); a key
+    column scores the sum of its softmax weights over those rows, a diagonal
+    i - j = o the sum along it; each head keeps the first `forced` columns and
+    offsets plus the highest-scoring others up to its budgets, ties to the
+    smaller index                                              [mizuki, 稀疏注意力 + 核优化]
 
 No function here is "parity unpinned": each is pinned by the CPU tests to
 closed forms, brute force, hand-worked fixtures or reductions to vanilla RoPE
@@ -322,3 +330,71 @@ def vanilla_prefill_rows(q_rows, rows, k, v, rope_base: float, yarn_scale: float
                     lse[b, h, r0:r0 + row_block] = ls
     return out, lse
 
+
+
+# ---------------------------------------------------------------------------
+# 5. Online vertical-slash estimation with continuous positions
+#    [mizuki, 稀疏注意力 + 核优化: the key-token selection stage restores
+#    continuous relative positions; 跟 NSA / 其他稀疏注意力的区别: a few key
+#    tokens draw most of the attention in a vertical-slash pattern]
+# ---------------------------------------------------------------------------
+
+def vs_scores(q_last, rows, k, rope_base: float, yarn_scale: float = 1.0, softmax_scale: float | None = None):
+    """Attention of the last query rows under continuous positions, summed
+    into per-head key-column and diagonal scores.
+
+    q_last [Hq, n, d]: the queries of rows `rows` ([n], ascending, the last n
+    rows of the sequence); k [Hkv, S, d] with S = rows[-1] + 1. The logits are
+    yarn * sigma * <R(i) q_i, R(j) k_j> -- RoPE at the true indices i and j,
+    not the DCA map -- causal (j <= i), one softmax per row. Returns
+    vertical [Hq, S] with vertical[h, j] = sum_i p_h[i, j], and slash [Hq, S]
+    with slash[h, o] = sum_i p_h[i, i - o] (o = i - j >= 0)."""
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    Hq, n, d = q_last.shape
+    Hkv, S, _ = k.shape
+    G = Hq // Hkv
+    sigma = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    scale = float(yarn_scale) * sigma
+    keys = torch.arange(S, dtype=torch.int64)
+    allowed = keys[None, :] <= rows[:, None]                       # [n, S]
+    vertical = torch.zeros((Hq, S), dtype=F64)
+    slash = torch.zeros((Hq, S), dtype=F64)
+    offs = rows[:, None] - keys[None, :]                           # i - j
+    for kvh in range(Hkv):
+        k_rot = rope_rotate(k[kvh], keys, rope_base)
+        for h in range(kvh * G, (kvh + 1) * G):
+            q_rot = rope_rotate(q_last[h], rows, rope_base)
+            logits = scale * (q_rot @ k_rot.T)
+            logits = torch.where(allowed, logits, torch.tensor(-math.inf, dtype=F64))
+            p = torch.softmax(logits, dim=-1)                      # rows sum to 1
+            vertical[h] = p.sum(dim=0)
+            slash[h].index_add_(0, offs[allowed], p[allowed])
+    return vertical, slash
+
+
+def top_with_forced(score, budget: int, forced: int):
+    """The indices [0, forced) (clipped to the array) plus the budget - forced
+    highest-scoring other indices, ties to the smaller index; ascending.
+    Every index is taken when there are fewer candidates than the budget."""
+    n = score.shape[0]
+    f = min(forced, budget, n)
+    head = torch.arange(f, dtype=torch.int64)
+    rest = torch.arange(f, n, dtype=torch.int64)
+    take = min(budget - f, rest.numel())
+    if take <= 0:
+        return head
+    # stable sort on the negated score: equal scores keep index order
+    order = torch.sort(-score[f:].to(F64), stable=True).indices[:take]
+    return torch.sort(torch.cat([head, rest[order]])).values
+
+
+def vs_estimate(q_last, rows, k, rope_base: float, n_vertical: int, n_slash: int, forced: int = 64,
+                yarn_scale: float = 1.0, softmax_scale: float | None = None):
+    """Per-head vertical columns and slash offsets for the vertical-slash mask:
+    the first `forced` columns and offsets always, the rest by score.
+    Returns (vertical [Hq, n_vertical'], slash [Hq, n_slash'], vscore, sscore)
+    as int64 / float64 tensors (n' = min(n, S))."""
+    vscore, sscore = vs_scores(q_last, rows, k, rope_base, yarn_scale, softmax_scale)
+    vert = torch.stack([top_with_forced(vscore[h], n_vertical, forced) for h in range(vscore.shape[0])])
+    sl = torch.stack([top_with_forced(sscore[h], n_slash, forced) for h in range(sscore.shape[0])])
+    return vert, sl, vscore, sscore

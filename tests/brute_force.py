@@ -73,3 +73,27 @@ def attention(q, k, v, C: int, W: int, base: float, tau: float, dist_fn=dca_dist
                 out[h, i] += (wj / tot) * v[kv, j]
             lse[h, i] = mx + math.log(tot)
     return out, lse
+
+
+def vs_scores(q_last, rows, k, base: float, tau: float):
+    """Column and diagonal sums of the attention of the rows `rows` under
+    continuous positions (distance i - j for every pair), from the pairwise
+    form of RoPE: q_last [Hq, n, d], k [Hkv, S, d] (numpy float64) ->
+    vertical [Hq, S], slash [Hq, S]."""
+    Hq, n, d = q_last.shape
+    Hkv, S, _ = k.shape
+    group = Hq // Hkv
+    th = theta(d, base)
+    vertical = np.zeros((Hq, S))
+    slash = np.zeros((Hq, S))
+    for h in range(Hq):
+        kv = h // group
+        for a, i in enumerate(rows):
+            lg = [tau / math.sqrt(d) * pair_logit(q_last[h, a], k[kv, j], i - j, th) for j in range(i + 1)]
+            mx = max(lg)
+            w = [math.exp(x - mx) for x in lg]
+            tot = sum(w)
+            for j in range(i + 1):
+                vertical[h, j] += w[j] / tot
+                slash[h, i - j] += w[j] / tot
+    return vertical, slash

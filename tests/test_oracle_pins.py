@@ -442,3 +442,77 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     spec.loader.exec_module(mod)
     assert _pins_pass(O)
     assert not _pins_pass(mod), f"planted mistake '{name}' not caught"
+
+
+# ---------------------------------------------------------------------------
+# online vertical-slash estimation (continuous positions)
+# ---------------------------------------------------------------------------
+
+def test_vs_scores_match_pairwise_brute_force():
+    Hq, Hkv, S, d, n = 4, 2, 90, 8, 12
+    q = _rand((Hq, n, d), 100)
+    k = _rand((Hkv, S, d), 101)
+    rows = torch.arange(S - n, S)
+    vs, ss = O.vs_scores(q, rows, k, 1e4, 1.3)
+    bv, bs = BF.vs_scores(q.numpy(), rows.tolist(), k.numpy(), 1e4, 1.3)
+    assert np.allclose(vs.numpy(), bv, rtol=0, atol=1e-12)
+    assert np.allclose(ss.numpy(), bs, rtol=0, atol=1e-12)
+    # every row's softmax sums to one
+    assert torch.allclose(vs.sum(1), torch.full((Hq,), float(n), dtype=F64), rtol=0, atol=1e-12)
+    assert torch.allclose(ss.sum(1), torch.full((Hq,), float(n), dtype=F64), rtol=0, atol=1e-12)
+
+
+def test_vs_scores_use_continuous_positions():
+    """The selection attention is vanilla RoPE attention: its per-row weights
+    reproduce the vanilla oracle's output, and differ from DCA's beyond one
+    chunk."""
+    Hq, Hkv, S, d, n = 2, 1, 160, 16, 4
+    q = _rand((1, Hq, S, d), 102)
+    k = _rand((1, Hkv, S, d), 103)
+    v = _rand((1, Hkv, S, d), 104)
+    rows = torch.arange(S - n, S)
+
+    def weights(run):
+        # V = a block of one-hot rows: the outputs are the attention weights
+        # of that block of keys
+        w = []
+        for c in range(S // d):
+            v = torch.zeros((1, Hkv, S, d), dtype=F64)
+            v[0, 0, c * d:(c + 1) * d] = torch.eye(d, dtype=F64)
+            w.append(run(v)[0])
+        return torch.cat(w, dim=-1)                                    # [Hq, n, S]
+
+    van = weights(lambda v: O.vanilla_prefill_rows(q[:, :, rows], rows, k, v, 1e4, 1.1)[0])
+    vs, _ = O.vs_scores(q[0, :, rows], rows, k[0], 1e4, 1.1)
+    assert torch.allclose(vs, van.sum(1), rtol=0, atol=1e-12)
+    dca = weights(lambda v: O.dca_prefill_rows(q[:, :, rows], rows, k, v, 32, 8, 1e4, 1.1)[0])
+    assert (dca.sum(1) - vs).abs().max() > 1e-3
+
+
+def test_vs_estimate_finds_planted_column_and_diagonal():
+    """Energy only in the slowest RoPE pair (angle below 1e-3 rad over the
+    sequence): a key 10x the query wins every row (a vertical), and keys 10x
+    the query at one fixed distance o* win along a diagonal (a slash)."""
+    S, d, n = 200, 16, 16
+    base = 1e7
+    rows = torch.arange(S - n, S)
+    unit = torch.zeros(d, dtype=F64)
+    unit[d // 2 - 1] = 0.3
+    q = unit.repeat(2, n, 1)
+    k = _rand((1, S, d), 105, 0.01)
+    k[0, 37] = 10 * unit
+    o_star = 77
+    for i in rows.tolist():
+        k[0, i - o_star] = 6 * unit
+    vert, sl, vs, ss = O.vs_estimate(q, rows, k, base, n_vertical=2, n_slash=2, forced=1)
+    assert vert[0].tolist() == [0, 37]
+    assert sl[0].tolist() == [0, o_star]
+
+
+def test_top_with_forced_ties_and_small_inputs():
+    score = torch.tensor([9.0, 1.0, 5.0, 5.0, 0.5, 5.0, 7.0], dtype=F64)
+    assert O.top_with_forced(score, 4, 2).tolist() == [0, 1, 2, 6]       # 7.0 then 5.0 at the smallest index
+    assert O.top_with_forced(score, 5, 2).tolist() == [0, 1, 2, 3, 6]
+    assert O.top_with_forced(score, 10, 2).tolist() == list(range(7))     # fewer candidates than the budget
+    assert O.top_with_forced(score, 3, 0).tolist() == [0, 2, 6]
+    assert O.top_with_forced(score, 1, 3).tolist() == [0]                 # forced clipped to the budget
