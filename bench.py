@@ -14,8 +14,9 @@ layer shape (dense causal work 4 d Hq S(S+1)/2); `roofline` reports the
 attention kernel against the bf16 dense MFMA peak; `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload; `extra` holds the other
 measured workloads: 128K dense, 1M vertical-slash, the 1M sequence as a
-chunked prefill in 32,768-row blocks, decode at a 1M context, and the 1M path
-with the query rotation fused into the attention kernel.
+chunked prefill in 32,768-row blocks, decode at a 1M context, the 1M path
+with the query rotation fused into the attention kernel, and the online
+vertical-slash estimate at 1M.
 """
 
 from __future__ import annotations
@@ -242,6 +243,43 @@ def measure_fused(name, device):
     return res
 
 
+def measure_estimate(name, device, n_vertical=1000, n_slash=2000, forced=64, n_last=64):
+    """Online vertical-slash estimation (dca_vs_estimate) on the workload's
+    shape: the last 64 query rows under continuous positions, per-head
+    budgets of the 1M vertical-slash workload."""
+    w = workloads.get(name)
+    log(f"[bench] generating inputs for {name} vertical-slash estimate")
+    q, k, v = synth.make_qkv(w, seed=0, device=device)
+    del v
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_vs_estimate_workspace_size(w.seq, shape)
+    ws = api.alloc_workspace(nbytes, device)
+    vert = torch.empty((w.n_q_heads, n_vertical), dtype=torch.int32, device=device)
+    slash = torch.empty((w.n_q_heads, n_slash), dtype=torch.int32, device=device)
+
+    def run():
+        api.dca_vs_estimate(q, k, w.seq, n_last, w.rope_base, w.yarn_scale, n_vertical, n_slash, forced, shape,
+                            vert, slash, None, None, ws, nbytes)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    # selection work: the scored rows' causal logits, twice (statistics, then sums)
+    flops = 2 * 4.0 * w.head_dim * w.n_q_heads * n_last * w.seq
+    res = {"workload": f"{name}_vs_estimate", "ms": ms, "n_last": n_last, "n_vertical": n_vertical,
+           "n_slash": n_slash, "tflops": flops / (ms * 1e-3) / 1e12}
+    log(f"[bench] {json.dumps(res)}")
+    del q, k, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_decode(name, steps, device):
     """DCA decode of the last `steps` tokens of the workload's sequence, one
     dca_decode call each, against the key/value cache of everything before
@@ -377,6 +415,7 @@ def main():
         extra.append(measure_chunked("qwen14b_1m", 32768, 1, 1, dev))
         extra.append(measure_decode("qwen14b_1m", 64, dev))
         extra.append(measure_fused("qwen14b_1m", dev))
+        extra.append(measure_estimate("qwen14b_1m", dev))
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]

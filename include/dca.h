@@ -176,6 +176,31 @@ int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, fl
                       const dca_vs_mask *mask, const dca_shape *shape,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Online vertical-slash estimation with continuous positions [mizuki,
+ * 稀疏注意力 + 核优化: key tokens are selected with the continuous relative
+ * positions restored; 跟 NSA / 其他稀疏注意力的区别: vertical-slash pattern].
+ * The last n_last (1..64) query rows of the sequence attend to every key with
+ * RoPE at the true indices i and j (not the DCA map) and the logit scale
+ * yarn_scale * softmax_scale; per query head, key column j scores the sum of
+ * its softmax weights over those rows and diagonal o = i - j the sum along
+ * it. Each head keeps columns [0, n_forced) plus the n_vertical - n_forced
+ * best other columns, and offsets [0, n_forced) plus the n_slash - n_forced
+ * best other offsets, ties to the smaller index. Batch must be 1
+ * (DCA_E_UNSUPPORTED). q: device [1][n_q_heads][seq][head_dim]; k: device
+ * [1][n_kv_heads][seq][head_dim]. vertical: device int32 [n_q_heads]
+ * [n_vertical], slash: device int32 [n_q_heads][n_slash], written ascending:
+ * ready to be a dca_vs_mask. vertical_score / slash_score: device float32
+ * [n_q_heads][seq] or NULL (then kept in the workspace). 1 <= n_vertical,
+ * n_slash <= seq and 0 <= n_forced <= both (DCA_E_INVALID). workspace: at
+ * least dca_vs_estimate_workspace_size bytes, 256-byte aligned; it holds the
+ * keys rotated at their own index and the reduction scratch. */
+int dca_vs_estimate_workspace_size(int64_t seq, const dca_shape *shape, size_t *bytes);
+int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, double rope_base,
+                    float yarn_scale, int32_t n_vertical, int32_t n_slash, int32_t n_forced,
+                    const dca_shape *shape, int32_t *vertical, int32_t *slash,
+                    float *vertical_score, float *slash_score, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* DCA decode of one new token per sequence [mizuki, Intra-/Successive-/
  * Inter-Chunk Attention, DCA + YaRN]: the token at sequence index pos (the
  * same for every batch entry) attends to the keys [0, pos] with the DCA

@@ -24,7 +24,7 @@ EXPORTS = [
     "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
     "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
     "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode", "dca_fused_workspace_size",
-    "dca_prefill_fused",
+    "dca_prefill_fused", "dca_vs_estimate_workspace_size", "dca_vs_estimate",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
 ]
 
@@ -65,6 +65,10 @@ _SIGS = {
     "dca_fused_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, ctypes.POINTER(ctypes.c_size_t)]),
     "dca_prefill_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, ctypes.c_double,
                                          ctypes.c_float, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_vs_estimate_workspace_size": (ctypes.c_int, [_I64, _VP, ctypes.POINTER(ctypes.c_size_t)]),
+    "dca_vs_estimate": (ctypes.c_int, [_VP, _VP, _I64, ctypes.c_int32, ctypes.c_double, ctypes.c_float,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, ctypes.c_size_t, _VP]),
     "dca_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float,
                                   _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
@@ -213,6 +217,21 @@ def dca_prefill_fused(q, k, v, out, lse, seq, C, W, rope_base, yarn_scale, mask,
                                    _stream(stream)), "dca_prefill_fused")
 
 
+def dca_vs_estimate_workspace_size(seq: int, shape: dca_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dca_vs_estimate_workspace_size(seq, ctypes.byref(shape), ctypes.byref(n)),
+           "dca_vs_estimate_workspace_size")
+    return n.value
+
+
+def dca_vs_estimate(q, k, seq, n_last, rope_base, yarn_scale, n_vertical, n_slash, n_forced, shape, vertical, slash,
+                    vertical_score, slash_score, workspace, workspace_bytes, stream=None):
+    _check(lib().dca_vs_estimate(_ptr(q), _ptr(k), seq, n_last, rope_base, yarn_scale, n_vertical, n_slash, n_forced,
+                                 ctypes.byref(shape), _ptr(vertical), _ptr(slash), _ptr(vertical_score),
+                                 _ptr(slash_score), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "dca_vs_estimate")
+
+
 def dca_decode(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
                stream=None):
     _check(lib().dca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pos, seq, C, W, rope_base, yarn_scale,
@@ -307,3 +326,22 @@ def prefill_chunked(q, k, v, C: int, W: int, chunk: int, rope_base: float = 1e7,
         if return_lse:
             lse[:, :, q0:q0 + n] = lc
     return (out, lse) if return_lse else out
+
+
+def vs_estimate(q, k, n_vertical: int, n_slash: int, n_forced: int = 64, n_last: int = 64, rope_base: float = 1e7,
+                yarn_scale: float = 1.0, softmax_scale: float = 0.0, return_scores: bool = False):
+    """Per-head vertical columns [Hq, n_vertical] and slash offsets [Hq, n_slash]
+    (int32, ascending, device) from the last n_last query rows under
+    continuous positions (dca_vs_estimate); batch 1."""
+    seq = q.shape[2]
+    shape = shape_of(q, k, softmax_scale)
+    nbytes = dca_vs_estimate_workspace_size(seq, shape)
+    ws = alloc_workspace(nbytes, q.device)
+    hq = q.shape[1]
+    vert = torch.empty((hq, n_vertical), dtype=torch.int32, device=q.device)
+    slash = torch.empty((hq, n_slash), dtype=torch.int32, device=q.device)
+    vs = torch.empty((hq, seq), dtype=torch.float32, device=q.device) if return_scores else None
+    ss = torch.empty((hq, seq), dtype=torch.float32, device=q.device) if return_scores else None
+    dca_vs_estimate(q, k, seq, n_last, rope_base, yarn_scale, n_vertical, n_slash, n_forced, shape, vert, slash, vs,
+                    ss, ws, nbytes)
+    return (vert, slash, vs, ss) if return_scores else (vert, slash)

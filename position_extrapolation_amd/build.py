@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdca.so")
-SOURCES = ["api.cpp", "remap.hip", "attention.hip", "vs_index.hip", "decode.hip"]
+SOURCES = ["api.cpp", "remap.hip", "attention.hip", "vs_index.hip", "decode.hip", "vs_estimate.hip"]
 ARCH = "gfx950"
 
 

@@ -51,7 +51,7 @@ Layout layout_for(const Problem &p) {
     L.table = take((size_t)p.n_pos * (size_t)(p.D / 2) * 8);
     const size_t kvbytes = (size_t)p.B * p.Hkv * p.S_pad * p.D * p.esize;
     L.k = take(kvbytes);
-    L.v = take(kvbytes);
+    L.v = take(p.keys_only ? 0 : kvbytes);
     if (p.sparse) {
         L.vs_flags = take((size_t)2 * p.Hq * p.n_tiles);
         L.vs_vt = take((size_t)p.Hq * p.n_tiles * 4);
@@ -376,6 +376,79 @@ int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, fl
     }
     const int err = launch_attention(p, out, lse, workspace, L, stream, q);
     if (err) return device_fail(err, "attention launch");
+    return ok();
+}
+
+// The estimate's workspace: the pre-pass layout for the keys rotated at their
+// own index (chunk length ceil(seq / 64) * 64 >= seq, window 0, keys only),
+// then the row statistics, then the two score arrays.
+static int est_problem(int64_t seq, const dca_shape *shape, Problem *p, size_t *scratch, size_t *scores,
+                       size_t *total) {
+    const int64_t C = (seq + kTile - 1) / kTile * kTile;
+    int st = make_problem(seq, C, 0, shape, nullptr, p);
+    if (st) return st;
+    if (p->B != 1) return fail(DCA_E_UNSUPPORTED, "the estimate takes batch 1 (got %lld)", (long long)p->B);
+    p->fused = true;
+    p->keys_only = true;
+    const size_t base = layout_for(*p).total;
+    *scratch = base;
+    *scores = align256(base + est_scratch_bytes(*p));
+    *total = align256(*scores + (size_t)2 * p->Hq * p->S * sizeof(float));
+    return DCA_OK;
+}
+
+int dca_vs_estimate_workspace_size(int64_t seq, const dca_shape *shape, size_t *bytes) {
+    if (bytes == nullptr) return fail(DCA_E_INVALID, "bytes is NULL");
+    Problem p;
+    size_t scratch, scores, total;
+    int st = est_problem(seq, shape, &p, &scratch, &scores, &total);
+    if (st) return st;
+    *bytes = total;
+    return ok();
+}
+
+int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, double rope_base, float yarn_scale,
+                    int32_t n_vertical, int32_t n_slash, int32_t n_forced, const dca_shape *shape,
+                    int32_t *vertical, int32_t *slash, float *vertical_score, float *slash_score,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    size_t scratch, scores, total;
+    int st = est_problem(seq, shape, &p, &scratch, &scores, &total);
+    if (st) return st;
+    if (q == nullptr || k == nullptr) return fail(DCA_E_INVALID, "q and k must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16)) return fail(DCA_E_INVALID, "q and k must be 16-byte aligned");
+    if (vertical == nullptr || slash == nullptr) return fail(DCA_E_INVALID, "vertical and slash must be non-NULL");
+    if (misaligned(vertical, 4) || misaligned(slash, 4) || misaligned(vertical_score, 4) || misaligned(slash_score, 4))
+        return fail(DCA_E_INVALID, "output lists and scores must be 4-byte aligned");
+    if (n_last < 1 || n_last > 64 || n_last > seq)
+        return fail(DCA_E_INVALID, "n_last must be in [1, min(64, seq)] (got %d)", n_last);
+    if (n_vertical < 1 || n_vertical > seq || n_slash < 1 || n_slash > seq)
+        return fail(DCA_E_INVALID, "budgets must be in [1, seq] (got %d, %d)", n_vertical, n_slash);
+    if (n_forced < 0 || n_forced > n_vertical || n_forced > n_slash)
+        return fail(DCA_E_INVALID, "n_forced must be in [0, min(budgets)] (got %d)", n_forced);
+    if ((st = check_rope(rope_base))) return st;
+    if ((st = check_yarn(yarn_scale))) return st;
+    if (workspace == nullptr) return fail(DCA_E_INVALID, "workspace is NULL");
+    if (((uintptr_t)workspace & 255) != 0) return fail(DCA_E_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < total)
+        return fail(DCA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    const Layout L = layout_for(p);
+    float *ws_scores = (float *)((char *)workspace + scores);   // [2][Hq][seq], used for absent outputs
+    float *vs = vertical_score ? vertical_score : ws_scores;
+    float *ss = slash_score ? slash_score : ws_scores + p.Hq * p.S;
+    const size_t vb = (size_t)p.Hq * n_vertical * 4, sb = (size_t)p.Hq * n_slash * 4, cb = (size_t)p.Hq * p.S * 4;
+    if (overlaps(vertical, vb, slash, sb) || overlaps(vertical, vb, workspace, workspace_bytes) ||
+        overlaps(slash, sb, workspace, workspace_bytes) || overlaps(vertical_score, cb, slash_score, cb))
+        return fail(DCA_E_INVALID, "outputs overlap each other or the workspace");
+    // keys rotated at their own index, scaled like the attention's
+    int err = launch_rope_table(p, rope_base, workspace, L, stream);
+    if (err) return device_fail(err, "rope table launch");
+    const float k_scale = yarn_scale * p.softmax_scale * 1.4426950408889634f;
+    err = launch_remap(p, nullptr, k, nullptr, k_scale, workspace, L, stream);
+    if (err) return device_fail(err, "key rotation launch");
+    err = launch_vs_estimate(p, n_last, n_vertical, n_slash, n_forced, q, workspace, L, scratch, vs, ss, vertical,
+                             slash, stream);
+    if (err) return device_fail(err, "vertical-slash estimate launch");
     return ok();
 }
 

@@ -56,6 +56,7 @@ struct Problem {
     float softmax_scale;
     bool sparse;
     bool fused;                      // queries rotated inside the attention kernel: no query section
+    bool keys_only;                  // no value section (rotated keys for the vertical-slash estimate)
     int32_t n_vertical, n_slash;
 };
 
@@ -111,6 +112,12 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
                   double rope_base, float k_scale, void *ws, const Layout &L, void *stream);
 size_t decode_scratch_bytes(const Problem &p);
+// online vertical-slash estimation over the keys rotated at their own index
+// (the pre-pass run with C >= S, W = 0, keys only)
+size_t est_scratch_bytes(const Problem &p);
+int launch_vs_estimate(const Problem &p, int n_last, int n_vertical, int n_slash, int n_forced, const void *q,
+                       const void *ws, const Layout &L, size_t scratch, float *vscore, float *sscore,
+                       int32_t *vertical, int32_t *slash, void *stream);
 int launch_debug_positions(int64_t S, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,
                            int32_t *pq_inter, int32_t *pk, void *stream);
 int launch_debug_tile_regions(int64_t S, int64_t C, uint8_t *out, void *stream);

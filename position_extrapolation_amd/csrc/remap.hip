@@ -61,7 +61,7 @@ struct RemapArgs {
     const float2 *table;
     float k_scale;               // multiplies the rotated keys
     int64_t n, q0, C, W;         // input rows per head, their first sequence index
-    int32_t Hq, Hkv;
+    int32_t Hq, Hkv, Hv;         // query, key and value heads handled (Hv = 0: keys only)
     int32_t nblk_q, nblk_kv;     // 32-row blocks per head in the query / key-value sections
     int32_t kv_blk_end;          // key-value blocks [q0 / 32, kv_blk_end) are written
 };
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
 
     const int64_t blk = blockIdx.x;
     const int y = blockIdx.y;
-    const int per_b = a.Hq + 2 * a.Hkv;
+    const int per_b = a.Hq + a.Hkv + a.Hv;
     const int b = y / per_b;
     const int hh = y % per_b;
     const int64_t kv_blk = a.q0 / kBlk + blk;     // the block's place in the key-value sections
@@ -191,10 +191,11 @@ static int launch_remap_t(const Problem &p, const void *q, const void *k, const 
     a.W = p.W;
     a.Hq = p.fused ? 0 : (int32_t)p.Hq;          // fused rotation: keys and values only
     a.Hkv = (int32_t)p.Hkv;
+    a.Hv = p.keys_only ? 0 : (int32_t)p.Hkv;
     a.nblk_q = (int32_t)(p.NQ_pad / kBlk);
     a.nblk_kv = (int32_t)(p.S_pad / kBlk);
     a.kv_blk_end = (int32_t)((p.q0 + p.NQ + kTile - 1) / kTile * (kTile / kBlk));
-    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (a.Hq + 2 * p.Hkv)));
+    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (a.Hq + a.Hkv + a.Hv)));
     hipLaunchKernelGGL((remap_kernel<T, D>), grid, dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }

@@ -194,6 +194,42 @@ def test_valid_decode_call_without_gpu_reports_device_error():
     assert _call_decode() == api.DCA_E_DEVICE
 
 
+def _call_estimate(**over):
+    sh = over.pop("shape", api.make_shape(1, 4, 2, 64, torch.float32))
+    args = dict(q=0x10000000, k=0x20000000, seq=2048, n_last=64, base=1e7, yarn=1.0, nv=100, ns=200, nf=64,
+                vert=0x30000000, slash=0x31000000, vs=None, ss=None, ws=0x50000000, ws_bytes=1 << 30)
+    args.update(over)
+    return api.lib().dca_vs_estimate(args["q"], args["k"], args["seq"], args["n_last"], args["base"], args["yarn"],
+                                     args["nv"], args["ns"], args["nf"], ctypes.byref(sh), args["vert"],
+                                     args["slash"], args["vs"], args["ss"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_last=0), api.DCA_E_INVALID),
+    (dict(n_last=65), api.DCA_E_INVALID),
+    (dict(nv=0), api.DCA_E_INVALID),
+    (dict(ns=4096), api.DCA_E_INVALID),                   # budget past the sequence
+    (dict(nf=101), api.DCA_E_INVALID),                    # forced past a budget
+    (dict(vert=None), api.DCA_E_INVALID),
+    (dict(shape=api.make_shape(2, 4, 2, 64, torch.float32)), api.DCA_E_UNSUPPORTED),   # batch 2
+    (dict(ws_bytes=1 << 20), api.DCA_E_WORKSPACE),
+    (dict(slash=0x30000000 + 64), api.DCA_E_INVALID),     # lists overlap
+])
+def test_estimate_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_estimate(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_estimate_workspace_size():
+    sh = api.make_shape(1, 40, 8, 128, torch.bfloat16)
+    S = 1 << 20
+    n = api.dca_vs_estimate_workspace_size(S, sh)
+    keys = 8 * S * 128 * 2
+    table = S * 64 * 8
+    scores = 2 * 40 * S * 4
+    assert keys + table + scores < n < keys + table + scores + (8 << 20)
+
+
 def test_status_strings():
     for s in range(5):
         assert api.dca_status_str(s).startswith("DCA_")

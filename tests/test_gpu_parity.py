@@ -547,3 +547,72 @@ def test_fused_rotation_vertical_slash():
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out)
     assert torch.equal(lse, ref_lse)
+
+
+# ---------------------------------------------------------------------------
+# online vertical-slash estimation (continuous positions)
+# ---------------------------------------------------------------------------
+
+def _est_case(dtype, Hq, Hkv, D, S, seed):
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, 64, 0, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    return w, synth.make_qkv(w, seed=seed, device=DEV)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,S,n_last,nv,ns,forced", [
+    ("bf16", 4, 2, 128, 3000, 64, 100, 200, 64),
+    ("f32", 3, 1, 64, 1000, 64, 50, 80, 16),
+    ("bf16", 2, 1, 64, 333, 20, 40, 333, 8),       # fewer rows, every offset kept
+    ("bf16", 5, 1, 128, 70, 64, 70, 10, 0),        # short sequence, no forced head
+])
+def test_vs_estimate_matches_oracle(dtype, Hq, Hkv, D, S, n_last, nv, ns, forced):
+    say(f"[vs estimate] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} n_last={n_last} nv={nv} ns={ns} forced={forced}")
+    w, (q, k, v) = _est_case(dtype, Hq, Hkv, D, S, seed=51)
+    tau = 1.1386294361
+    vert, slash, vs, ss = api.vs_estimate(q, k, nv, ns, forced, n_last, 1e7, tau, return_scores=True)
+    torch.cuda.synchronize()
+    rows = torch.arange(S - n_last, S)
+    ref_v, ref_s, ref_vs, ref_ss = O.vs_estimate(q[0, :, rows].cpu(), rows, k[0].cpu(), 1e7, nv, ns, forced, tau)
+    ev = (vs.double().cpu() - ref_vs).abs().max().item()
+    es = (ss.double().cpu() - ref_ss).abs().max().item()
+    say(f"  score err vertical={ev:.3e} slash={es:.3e}")
+    tol = TOL[dtype]
+    assert ev <= tol and es <= tol
+    # the lists are exactly the selection the rule makes on the kernel's own scores
+    for h in range(Hq):
+        assert vert[h].cpu().long().tolist() == O.top_with_forced(vs[h].double().cpu(), nv, forced).tolist()
+        assert slash[h].cpu().long().tolist() == O.top_with_forced(ss[h].double().cpu(), ns, forced).tolist()
+        # and differ from the oracle's only on near-ties at the budget's edge
+        for got, ref, sc in ((vert[h], ref_v[h], ref_vs[h]), (slash[h], ref_s[h], ref_ss[h])):
+            a, b = set(got.cpu().tolist()), set(ref.tolist())
+            if a == b:
+                continue
+            edge = min(float(sc[i]) for i in b if i >= forced)
+            for i in a ^ b:
+                assert abs(float(sc[i]) - edge) <= 2 * tol, (h, i)
+
+
+def test_vs_estimate_finds_planted_pattern_and_drives_sparse_prefill():
+    """Keys planted along a column and along a diagonal are found at a
+    16K-token sequence, and the lists drive the sparse prefill."""
+    S, Hq, Hkv, D = 16384, 2, 1, 128
+    say(f"[vs estimate planted] S={S}")
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, 4096, 512, "bf16", 0.5, True)
+    q, k, v = synth.make_qkv(w, seed=52, device=DEV)
+    # energy only in the slowest RoPE pair: the logits are nearly position-free
+    unit = torch.zeros(D, device=DEV)
+    unit[D // 2 - 1] = 1.0
+    q[:, :, S - 64:] = (unit * 0.5).to(q.dtype)
+    k[0, 0, 5000] = (unit * 12).to(k.dtype)
+    o_star = 9000
+    for i in range(S - 64, S):
+        k[0, 0, i - o_star] = (unit * 8).to(k.dtype)
+    vert, slash = api.vs_estimate(q, k, 200, 400, 64)
+    torch.cuda.synchronize()
+    for h in range(Hq):
+        assert 5000 in vert[h].tolist()
+        assert o_star in slash[h].tolist()
+    out = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, vertical=vert, slash=slash)
+    torch.cuda.synchronize()
+    rows = np.array([S - 1, S - 30, 12000, 700])
+    ref, _ = _oracle(q, k, v, rows, w, vertical=vert.cpu().long(), slash=slash.cpu().long())
+    assert _err(out[:, :, torch.as_tensor(rows, device=DEV)], ref) <= TOL["bf16"]
