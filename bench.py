@@ -385,7 +385,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen14b_1m")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the 128K, vertical-slash and chunked-prefill workloads")
+                    help="skip the extra workloads (128K, vertical-slash, chunked, decode, fused, estimate)")
+    ap.add_argument("--only", choices=["decode", "chunked", "fused", "estimate"],
+                    help="run just this 1M measurement and print its JSON (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -402,6 +404,13 @@ def main():
     dev = "cuda:0"
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, dev)
+        return
+    if args.only:
+        run = {"decode": lambda: measure_decode("qwen14b_1m", 64, dev),
+               "chunked": lambda: measure_chunked("qwen14b_1m", 32768, 1, 0, dev),
+               "fused": lambda: measure_fused("qwen14b_1m", dev),
+               "estimate": lambda: measure_estimate("qwen14b_1m", dev)}[args.only]
+        print(json.dumps(run()), flush=True)
         return
     api.lib()
 
