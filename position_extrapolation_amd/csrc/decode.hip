@@ -212,14 +212,16 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void decode_attn_kernel
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid B * Hq blocks of 256 threads (one per split slot)
+// combine: grid B * Hq blocks of 1024 threads
 // ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kMaxSplits) void decode_combine_kernel(DecodeArgs a) {
-    constexpr int NT = kMaxSplits;
-    constexpr int RPT = NT / D;                  // threads sharing one output element
-    __shared__ float wgt[NT];                    // 2^(m_s - M), 0 for empty splits
-    __shared__ float red[NT];
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int RPT = kCombineThreads / D;     // threads sharing one output element
+    static_assert(kMaxSplits <= kCombineThreads, "one thread per split for the reductions");
+    __shared__ float wgt[kMaxSplits];            // 2^(m_s - M), 0 for empty splits
+    __shared__ float red[kCombineThreads];
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
     const float *part = a.part + bh * kMaxSplits * (D + 2);
@@ -228,17 +230,17 @@ __global__ __launch_bounds__(kMaxSplits) void decode_combine_kernel(DecodeArgs a
     // M = max over the live splits
     red[t] = m;
     __syncthreads();
-    for (int w = NT / 2; w > 0; w /= 2) {
+    for (int w = kCombineThreads / 2; w > 0; w /= 2) {
         if (t < w) red[t] = fmaxf(red[t], red[t + w]);
         __syncthreads();
     }
     const float mx = red[0];
     __syncthreads();
     const float wt = live ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
-    wgt[t] = wt;
+    if (t < kMaxSplits) wgt[t] = wt;
     red[t] = live ? wt * part[t * (D + 2) + D + 1] : 0.f;
     __syncthreads();
-    for (int w = NT / 2; w > 0; w /= 2) {
+    for (int w = kCombineThreads / 2; w > 0; w /= 2) {
         if (t < w) red[t] += red[t + w];
         __syncthreads();
     }
@@ -250,9 +252,12 @@ __global__ __launch_bounds__(kMaxSplits) void decode_combine_kernel(DecodeArgs a
     for (int s = r; s < a.n_split; s += RPT) num += wgt[s] * part[s * (D + 2) + d];
     red[t] = num;
     __syncthreads();
+    for (int w = RPT / 2; w > 0; w /= 2) {
+        if (r < w) red[t] += red[t + w * D];
+        __syncthreads();
+    }
     if (r == 0) {
-        for (int i = 1; i < RPT; ++i) num += red[i * D + d];
-        ((T *)a.out)[bh * D + d] = Frag<T>::from_float(den > 0.f ? num / den : 0.f);
+        ((T *)a.out)[bh * D + d] = Frag<T>::from_float(den > 0.f ? red[d] / den : 0.f);
         if (a.lse != nullptr && d == 0)
             a.lse[bh] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
     }
@@ -296,7 +301,7 @@ static int launch_decode_t(const Problem &p, const void *q, const void *k, const
     hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3((unsigned)a.n_split, (unsigned)groups), dim3(64), 0, s, a);
     err = (int)hipGetLastError();
     if (err) return err;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(p.B * p.Hq)), dim3(kMaxSplits), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(p.B * p.Hq)), dim3(kCombineThreads), 0, s, a);
     return (int)hipGetLastError();
 }
 
