@@ -28,6 +28,12 @@
 // streams so that the workgroups resident on one XCD (workgroup i lands on
 // XCD i mod 8) share one KV head and sweep the same keys through that XCD's
 // L2.
+//
+// A launch computes the rows [q0, q0 + NQ) of the sequence (a whole-sequence
+// prefill, or one block of a chunked prefill [mizuki, Chunked Prefill]) with
+// the keys kept at their sequence positions. With FUSED, each wave reads its
+// rows of the caller's queries and rotates them itself when it enters a
+// region, instead of reading the pre-pass's rotated variants.
 #include <hip/hip_runtime.h>
 
 #include "dca_internal.h"
