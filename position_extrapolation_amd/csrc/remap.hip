@@ -48,9 +48,9 @@ int launch_rope_table(const Problem &p, double rope_base, void *ws, const Layout
 // ---------------------------------------------------------------------------
 // remap kernel
 // The inputs hold the n rows [q0, q0 + n) of the sequence (q0 = 0, n = S for a
-// whole-sequence call). grid.x = ceil(n / 256) * 8 row blocks of 32; grid.y =
-// B * (Hq + Hkv + Hkv): query heads, then key heads (rotated), then value
-// heads (re-laid out). Query variants are written at the call's own row
+// whole-sequence call). grid.x = B * (Hq + Hkv + Hkv): query heads, then key
+// heads (rotated), then value heads (re-laid out); grid.y = ceil(n / 256) * 8
+// row blocks of 32. Query variants are written at the call's own row
 // blocks; keys and values at their blocks in the sequence, up to the end of
 // the last 64-key tile the call's rows can see (rows past n as zeros).
 // ---------------------------------------------------------------------------
@@ -75,8 +75,10 @@ __global__ __launch_bounds__(256) void remap_kernel(RemapArgs a) {
     constexpr int HALF = D / 2;
     constexpr int BLK_ELEMS = kBlk * D;
 
-    const int64_t blk = blockIdx.x;
-    const int y = blockIdx.y;
+    // heads vary fastest: the workgroups of one row block, which read the
+    // same table rows, run together and share them through L2
+    const int64_t blk = blockIdx.y;
+    const int y = blockIdx.x;
     const int per_b = a.Hq + a.Hkv + a.Hv;
     const int b = y / per_b;
     const int hh = y % per_b;
@@ -195,7 +197,7 @@ static int launch_remap_t(const Problem &p, const void *q, const void *k, const 
     a.nblk_q = (int32_t)(p.NQ_pad / kBlk);
     a.nblk_kv = (int32_t)(p.S_pad / kBlk);
     a.kv_blk_end = (int32_t)((p.q0 + p.NQ + kTile - 1) / kTile * (kTile / kBlk));
-    dim3 grid((unsigned)(p.NQ_pad / kBlk), (unsigned)(p.B * (a.Hq + a.Hkv + a.Hv)));
+    dim3 grid((unsigned)(p.B * (a.Hq + a.Hkv + a.Hv)), (unsigned)(p.NQ_pad / kBlk));
     hipLaunchKernelGGL((remap_kernel<T, D>), grid, dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
