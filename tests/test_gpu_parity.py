@@ -221,6 +221,43 @@ def test_parity_sampled_rows(name):
     _discrimination(q, k, v, rows, w, ref, out[:, :, rows_t])
 
 
+def test_parity_sampled_rows_1m():
+    """The 1M-token Qwen2.5-14B shape in the launch configuration the
+    benchmark times: the oracle on the forced boundary rows plus seeded rows
+    (32 rows x 40 heads keeps the float64 oracle near half a minute)."""
+    w = workloads.get("qwen14b_1m")
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, 32, seed=0)
+    say(f"[parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
+    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    out, lse = _run(q, k, v, w)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    out_rows, lse_rows = out[:, :, rows_t].clone(), lse[:, :, rows_t].clone()
+    del out, lse
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err, lerr = _err(out_rows, ref), _err(lse_rows, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    _discrimination(q, k, v, rows, w, ref, out_rows)
+
+
+def test_vs_parity_1m():
+    """The 1M vertical-slash workload (1000 columns, 2000 offsets per head)
+    on sampled rows."""
+    w = workloads.get("qwen14b_1m_vs")
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, 24, seed=1)
+    say(f"[vs parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
+    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    vert, slash = _vs_case(w, seed=0)
+    out, lse = _run(q, k, v, w, vertical=vert.to(DEV), slash=slash.to(DEV))
+    rows_t = torch.as_tensor(rows, device=DEV)
+    out_rows, lse_rows = out[:, :, rows_t].clone(), lse[:, :, rows_t].clone()
+    del out, lse
+    ref, ref_lse = _oracle(q, k, v, rows, w, vertical=vert, slash=slash)
+    err, lerr = _err(out_rows, ref), _err(lse_rows, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+
+
 def test_planted_needles_bf16():
     """For chosen rows, overwrite one key so that its rotated copy is a large
     multiple of the row's rotated query under the pair's region; the output of
