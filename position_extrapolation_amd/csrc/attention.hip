@@ -27,7 +27,7 @@
 // Grid order: heaviest row tiles first; the work list is cut into per-XCD
 // streams so that the workgroups resident on one XCD (workgroup i lands on
 // XCD i mod 8) share one KV head and sweep the same keys through that XCD's
-// L2.
+// L2. Vertical-slash launches are ordered differently (kSparseGeneration).
 //
 // A launch computes the rows [q0, q0 + NQ) of the sequence (a whole-sequence
 // prefill, or one block of a chunked prefill [mizuki, Chunked Prefill]) with
@@ -55,7 +55,7 @@ struct AttnArgs {
     int32_t Hq, Hkv, G;
     int32_t nblk_q, nblk_kv;     // 32-row blocks per head in the query / key-value sections
     // work decode
-    int32_t n_rt, KVH, s_split, M, per_xcd;
+    int32_t n_rt, KVH, s_split, M, per_xcd, rgen;
     // vertical-slash lists
     const int32_t *vt, *vt_n, *dl, *dl_n;
     int32_t list_stride;
@@ -63,6 +63,16 @@ struct AttnArgs {
 };
 
 constexpr int kNone = 0x7fffffff;
+
+// Vertical-slash grid order. The work is cut into units of this many
+// adjacent row tiles of one query head (about the workgroups one XCD holds at
+// once); units are dealt round-robin to the XCDs, KV group by KV group. The
+// workgroups running together on an XCD then share their head's vertical
+// tiles and many slash tiles through its L2, and all XCDs read the keys of
+// one KV group, whose recently used tiles the memory-side cache keeps. Dense
+// launches keep the query heads of a KV group together on an XCD instead
+// (every workgroup reads every key).
+constexpr int kSparseGeneration = 64;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -273,14 +283,28 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     const int bid = blockIdx.x;
     const int xcd = bid % kXcds;
     const int slot = bid / kXcds;
-    const int gg = slot % a.G;
-    const int mm = (slot / a.G) % a.M;
-    const int tt = slot / (a.G * a.M);
-    const int sigma = xcd + kXcds * mm;
-    const int kvg = sigma % a.KVH;
-    const int kres = sigma / a.KVH;
-    const int rt_desc = kres + a.s_split * tt;
-    if (slot >= a.per_xcd || rt_desc >= a.n_rt) return;
+    int gg, kvg, rt_desc;
+    if (a.sparse) {
+        // generation units u = (kv group, row-tile block, query head), dealt
+        // round-robin to the XCDs so that all XCDs work on one KV group
+        const int inner = slot % a.rgen;
+        const int u = (slot / a.rgen) * kXcds + xcd;
+        const int nrblk = (a.n_rt + a.rgen - 1) / a.rgen;
+        kvg = u / (nrblk * a.G);
+        const int rem = u % (nrblk * a.G);
+        gg = rem % a.G;
+        rt_desc = (rem / a.G) * a.rgen + inner;
+        if (slot >= a.per_xcd || kvg >= a.KVH || rt_desc >= a.n_rt) return;
+    } else {
+        gg = slot % a.G;
+        const int mm = (slot / a.G) % a.M;
+        const int tt = slot / (a.G * a.M);
+        const int sigma = xcd + kXcds * mm;
+        kvg = sigma % a.KVH;
+        const int kres = sigma / a.KVH;
+        rt_desc = kres + a.s_split * tt;
+        if (slot >= a.per_xcd || rt_desc >= a.n_rt) return;
+    }
     const int rt = a.n_rt - 1 - rt_desc;
     const int b = kvg / a.Hkv;
     const int kvh = kvg % a.Hkv;
@@ -422,7 +446,13 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     a.s_split = kXcds / gcd;
     a.M = a.KVH / gcd;
     const int64_t per_stream = (a.n_rt + a.s_split - 1) / a.s_split;
-    a.per_xcd = (int32_t)(per_stream * a.M * a.G);
+    a.rgen = a.sparse ? kSparseGeneration : 1;
+    if (a.sparse) {
+        const int64_t units = (int64_t)a.KVH * a.G * ((a.n_rt + a.rgen - 1) / a.rgen);
+        a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds * a.rgen);
+    } else {
+        a.per_xcd = (int32_t)(per_stream * a.M * a.G);
+    }
     const int64_t grid = (int64_t)a.per_xcd * kXcds;
     const int lds_bytes = NS * 2 * (2 * kBlk * D * (int)sizeof(T));   // NS slots of [K tile | V tile]
     auto kern = a.q_nat != nullptr ? dca_attention_kernel<T, D, NW, NS, TPS, true>
