@@ -16,6 +16,8 @@
 // cores in base-2 exponent units):
 //   est_rowstat_kernel   one wave per (split of the key tiles, head, 32-row
 //                        block): S^T = K Q^T, running max and sum per row;
+//                        the waves of one KV head and split run together on
+//                        one XCD (est_decode) and share the key tiles in L2;
 //   est_rowcombine_kernel  row max M and 1 / sum per row over the splits;
 //   est_clear_kernel     zeroes the diagonal scores;
 //   est_sums_kernel      one wave per (split, head): S = Q K^T for all rows,
@@ -26,8 +28,10 @@
 //                        atomically to zero: the result does not depend on
 //                        their order;
 //   est_topk_kernel      per (head, list): radix select of the budget's
-//                        threshold on the scores' bits, then an index-ordered
-//                        compaction (ties to the smaller index).
+//                        threshold on the scores' bits (histogram adds
+//                        grouped per wave and bin), then an index-ordered
+//                        compaction, 8192 scores per step, placed by one
+//                        block scan (ties to the smaller index).
 #include <hip/hip_runtime.h>
 
 #include "dca_internal.h"
@@ -37,6 +41,8 @@ namespace dca {
 
 constexpr int kEstRows = 64;          // query rows scored: the last n <= 64
 constexpr int kEstMaxSplits = 256;
+constexpr int64_t kEstRowstatWaves = 8192;   // targets for the two score passes
+constexpr int64_t kEstSumsWaves = 4096;
 
 struct EstArgs {
     const void *q;                   // [Hq][S][D], batch 1
@@ -49,7 +55,23 @@ struct EstArgs {
     int32_t Hq, Hkv, G, nblk_kv;
     int32_t r0;                      // first scored row, S - n
     int32_t n_split, tiles_per_split, n_tiles;
+    int32_t n_sets;                  // (KV head, split) pairs: the waves of a set read the same key tiles
 };
+
+// 1D grids: the waves that read the same key tiles -- one (KV head, split)
+// set, `members` waves -- are consecutive workgroups of one XCD (workgroup i
+// runs on XCD i mod 8), so the tiles come from HBM once per set and then
+// from that XCD's L2. Returns false for the padding workgroups of the grid.
+__device__ __forceinline__ bool est_decode(const EstArgs &a, int members, int &kvh, int &split, int &member) {
+    const int bid = blockIdx.x;
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    member = slot % members;
+    const int set = (slot / members) * kXcds + xcd;
+    if (set >= a.n_sets) return false;
+    kvh = set / a.n_split;
+    split = set % a.n_split;
+    return true;
+}
 
 __device__ inline float est_swap32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -91,11 +113,11 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
     constexpr int NU = D / (2 * F::E);
     constexpr int BLK_ELEMS = kBlk * D;
     constexpr int TILE_BYTES = 2 * BLK_ELEMS * (int)sizeof(T);
-    const int split = blockIdx.x;
-    const int h = blockIdx.y / 2, rb = blockIdx.y % 2;
+    int kvh, split, member;
+    if (!est_decode(a, 2 * a.G, kvh, split, member)) return;
+    const int h = kvh * a.G + member / 2, rb = member % 2;
     const int lane = threadIdx.x, x = lane % 32, g = lane / 32;
     const int64_t row = (int64_t)a.r0 + kBlk * rb + x;
-    const int kvh = h / a.G;
     vec qf[NU];
     est_load_q<T, D>(a, h, rb, lane, qf);
     const char *kbase = (const char *)a.kf + (int64_t)kvh * a.nblk_kv * BLK_ELEMS * (int64_t)sizeof(T);
@@ -171,9 +193,10 @@ __global__ __launch_bounds__(64) void est_sums_kernel(EstArgs a) {
     constexpr int TILE_BYTES = 2 * BLK_ELEMS * (int)sizeof(T);
     constexpr int LD = kTile + 1;                      // padded LDS row
     __shared__ float P[kEstRows * LD];                 // weights: [row - r0][key - j0]
-    const int split = blockIdx.x, h = blockIdx.y;
+    int kvh, split, member;
+    if (!est_decode(a, a.G, kvh, split, member)) return;
+    const int h = kvh * a.G + member;
     const int lane = threadIdx.x, x = lane % 32, g = lane / 32;
-    const int kvh = h / a.G;
     vec qf[2][NU];
     est_load_q<T, D>(a, h, 0, lane, qf[0]);
     est_load_q<T, D>(a, h, 1, lane, qf[1]);
@@ -220,15 +243,21 @@ __global__ __launch_bounds__(64) void est_sums_kernel(EstArgs a) {
             if (g == 0 && j < a.S) vs[j] = col;
         }
         __syncthreads();
-        // diagonal sums of the tile: lane t takes a - b = t and a - b = -t
-        // (a = row - r0, b = key - j0), i.e. offsets (r0 - j0) + t and (r0 - j0) - t
+        // diagonal sums of the tile (a = row - r0, b = key - j0): lane t reads
+        // P[r][(r - t) mod 64] for every r, which is diagonal a - b = t for
+        // r >= t and a - b = t - 64 for r < t; the diagonal offset of a - b = d
+        // is (r0 - j0) + d
         const int t = lane;
         float dp = 0.f, dm = 0.f;
-        for (int r = t; r < kEstRows; ++r) dp += P[r * LD + (r - t)];
-        for (int r = 0; r + t < kTile; ++r) dm += P[r * LD + (r + t)];
+#pragma unroll
+        for (int r = 0; r < kEstRows; ++r) {
+            const float w = P[r * LD + ((r - t) & (kTile - 1))];
+            if (r >= t) dp += w; else dm += w;
+        }
         const int64_t base = (int64_t)a.r0 - j0;
         if (base + t >= 0 && base + t < a.S && dp != 0.f) atomicAdd(&ss[base + t], dp);
-        if (t > 0 && base - t >= 0 && base - t < a.S && dm != 0.f) atomicAdd(&ss[base - t], dm);
+        const int64_t om = base + t - kTile;
+        if (t > 0 && om >= 0 && om < a.S && dm != 0.f) atomicAdd(&ss[om], dm);
         __syncthreads();
     }
 }
@@ -275,10 +304,32 @@ struct TopkArgs {
     int64_t S;
 };
 
+constexpr int kTopkPer = 8;                          // elements per thread and step
+constexpr int kTopkStep = kTopkThreads * kTopkPer;
+
+// hist[bin] += 1 for the valid lanes. The scores crowd into a few bins, so
+// the lanes of a wave that share a bin add once, with their count (up to four
+// distinct bins per call; the remaining lanes add one by one).
+__device__ __forceinline__ void hist_add(unsigned *hist, unsigned bin, bool valid) {
+    const int lane = threadIdx.x % 64;
+    uint64_t pending = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (pending == 0) break;
+        const int leader = __builtin_ctzll(pending);
+        const unsigned lb = (unsigned)__builtin_amdgcn_readlane((int)bin, leader);
+        const uint64_t same = __builtin_amdgcn_ballot_w64(valid && bin == lb) & pending;
+        if (lane == leader) atomicAdd(&hist[lb], (unsigned)__builtin_popcountll(same));
+        pending &= ~same;
+    }
+    if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
 __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
     __shared__ unsigned hist[256];
     __shared__ int wsum[kTopkThreads / 64];
     __shared__ unsigned sel_bin, sel_above;
+    __shared__ unsigned stage[kTopkStep];
     const int h = blockIdx.x, list = blockIdx.y;
     const int tid = threadIdx.x;
     const int64_t n = a.S;
@@ -299,9 +350,18 @@ __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
-        for (int64_t i = f + tid; i < n; i += kTopkThreads) {
-            const unsigned b = bits[i];
-            if ((b & pmask) == prefix) atomicAdd(&hist[(b >> shift) & 255u], 1u);
+        for (int64_t b0 = f; b0 < n; b0 += kTopkStep) {
+            unsigned v[kTopkPer];
+#pragma unroll
+            for (int e = 0; e < kTopkPer; ++e) {
+                const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
+                v[e] = i < n ? bits[i] : 0u;
+            }
+#pragma unroll
+            for (int e = 0; e < kTopkPer; ++e) {
+                const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
+                hist_add(hist, (v[e] >> shift) & 255u, i < n && (v[e] & pmask) == prefix);
+            }
         }
         __syncthreads();
         if (tid == 0) {
@@ -321,23 +381,49 @@ __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
         __syncthreads();
     }
     // bits > prefix are all taken; `remaining` of the bits == prefix, the
-    // smallest indices first; written in index order after the forced head
+    // smallest indices first; written in index order after the forced head.
+    // Per step, thread t owns the kTopkPer consecutive indices b0 + 8t ..; one
+    // scan of its packed (greater, equal) counts places all of its picks.
+    const int R = (int)remaining;
     int pos = f;
-    int ties = 0;
-    for (int64_t base = f; base < n; base += kTopkThreads) {
-        const int64_t i = base + tid;
-        const unsigned b = i < n ? bits[i] : 0u;
-        const bool gt = i < n && b > prefix;
-        const bool eq = i < n && b == prefix;
-        int eq_total;
-        const int eq_rank = block_scan(eq ? 1 : 0, &eq_total, wsum) - (eq ? 1 : 0);
-        const bool take = gt || (eq && ties + eq_rank < (int)remaining);
-        int tot;
-        const int rank = block_scan(take ? 1 : 0, &tot, wsum) - (take ? 1 : 0);
-        if (take) out[pos + rank] = (int32_t)i;
-        pos += tot;
-        ties += eq_total;
-        if (pos >= budget) break;
+    int ties = 0;                                      // equal bits seen before this step
+    for (int64_t b0 = f; b0 < n && pos < budget; b0 += kTopkStep) {
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+            const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
+            stage[e * kTopkThreads + tid] = i < n ? bits[i] : 0u;
+        }
+        __syncthreads();
+        unsigned w[kTopkPer];
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+            w[e] = stage[kTopkPer * tid + e];
+            const bool valid = b0 + kTopkPer * tid + e < n;
+            gt += valid && w[e] > prefix;
+            eq += valid && w[e] == prefix;
+        }
+        const int packed = gt | (eq << 16);            // both < 2^16: no carry between the halves
+        int total;
+        const int excl = block_scan(packed, &total, wsum) - packed;
+        const int r_left = max(R - ties, 0);           // equal bits still to take
+        int eq_seen = excl >> 16;
+        int o = pos + (excl & 0xffff) + min(eq_seen, r_left);
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+            const int64_t i = b0 + kTopkPer * tid + e;
+            if (i >= n) break;
+            bool take = w[e] > prefix;
+            if (w[e] == prefix) {
+                take = eq_seen < r_left;
+                ++eq_seen;
+            }
+            if (take) out[o++] = (int32_t)i;
+        }
+        const int tot_gt = total & 0xffff, tot_eq = total >> 16;
+        pos += tot_gt + min(tot_eq, r_left);
+        ties += tot_eq;
+        __syncthreads();                               // stage is rewritten next step
     }
 }
 
@@ -362,21 +448,36 @@ static int launch_est_t(const Problem &p, int n_last, const void *q, const void 
     a.nblk_kv = (int32_t)(p.S_pad / kBlk);
     a.r0 = (int32_t)(p.S - n_last);
     a.n_tiles = (int32_t)((p.S + kTile - 1) / kTile);
-    int64_t want = (2048 + p.Hq - 1) / p.Hq;
-    want = want < kEstMaxSplits ? want : kEstMaxSplits;
-    want = want < a.n_tiles ? want : a.n_tiles;
-    a.tiles_per_split = (int32_t)((a.n_tiles + want - 1) / want);
-    a.n_split = (a.n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+    auto set_splits = [&](EstArgs &e, int64_t waves_target, int members_per_set) {
+        int64_t want = waves_target / (p.Hkv * members_per_set);
+        want = want < 1 ? 1 : want;
+        want = want < kEstMaxSplits ? want : kEstMaxSplits;
+        want = want < e.n_tiles ? want : e.n_tiles;
+        e.tiles_per_split = (int32_t)((e.n_tiles + want - 1) / want);
+        e.n_split = (e.n_tiles + e.tiles_per_split - 1) / e.tiles_per_split;
+        e.n_sets = (int32_t)(p.Hkv * e.n_split);
+    };
+    // many more waves than fit at once, so that no pass ends on a thin last round
+    EstArgs ar = a;
+    set_splits(ar, kEstRowstatWaves, 2 * (int)p.G);
+    set_splits(a, kEstSumsWaves, (int)p.G);
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL((est_rowstat_kernel<T, D>), dim3((unsigned)a.n_split, (unsigned)(2 * p.Hq)), dim3(64), 0, s, a);
+    const int64_t rows_r = (ar.n_sets + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((est_rowstat_kernel<T, D>), dim3((unsigned)(rows_r * 2 * p.G)), dim3(64), 0, s, ar);
     int err = (int)hipGetLastError();
     if (err) return err;
+    const int64_t set_rows = (a.n_sets + kXcds - 1) / kXcds * kXcds;
+    a.n_split = ar.n_split;      // the row combine reads the row-statistics splits
     hipLaunchKernelGGL(est_rowcombine_kernel, dim3((unsigned)p.Hq), dim3(kEstRows), 0, s, a);
     if ((err = (int)hipGetLastError())) return err;
     const int64_t n = p.Hq * p.S;
     hipLaunchKernelGGL(est_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, sscore, n);
     if ((err = (int)hipGetLastError())) return err;
-    hipLaunchKernelGGL((est_sums_kernel<T, D>), dim3((unsigned)a.n_split, (unsigned)p.Hq), dim3(64), 0, s, a);
+    {
+        EstArgs as = a;
+        set_splits(as, kEstSumsWaves, (int)p.G);
+        hipLaunchKernelGGL((est_sums_kernel<T, D>), dim3((unsigned)(set_rows * p.G)), dim3(64), 0, s, as);
+    }
     return (int)hipGetLastError();
 }
 

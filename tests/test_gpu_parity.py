@@ -628,6 +628,43 @@ def test_vs_estimate_matches_oracle(dtype, Hq, Hkv, D, S, n_last, nv, ns, forced
                 assert abs(float(sc[i]) - edge) <= 2 * tol, (h, i)
 
 
+def test_vs_estimate_ties_across_compaction_steps():
+    """A 50K-token sequence (the selection compacts several 8192-score steps)
+    with ~13K zeroed keys: their columns score exactly alike, and the
+    vertical budget is set so that its edge falls inside that run of ties.
+    The lists must be exactly the selection rule on the kernel's own scores
+    (ties to the smaller index), and the scores match the oracle's."""
+    S, Hq, Hkv, D, n_last, forced = 50000, 2, 1, 64, 64, 64
+    say(f"[vs estimate ties] S={S}")
+    w, (q, k, v) = _est_case("bf16", Hq, Hkv, D, S, seed=53)
+    k[0, 0, 1000:40000:3] = 0
+    tied = torch.arange(1000, 40000, 3)
+    _, _, vs, _ = api.vs_estimate(q, k, 100, 100, forced, n_last, 1e7, 1.0, return_scores=True)
+    torch.cuda.synchronize()
+    vsc = vs.double().cpu()
+    # the zeroed columns share one score per head; budget = forced + (columns
+    # above it) + half of the tied run
+    nvs = []
+    for h in range(Hq):
+        c0 = vsc[h, tied]
+        assert torch.equal(c0, c0[:1].expand_as(c0)), "zeroed keys must tie exactly"
+        above = int((vsc[h, forced:] > c0[0]).sum())
+        nvs.append(forced + above + tied.numel() // 2)
+    nv = max(nvs)
+    vert, slash, vs2, ss2 = api.vs_estimate(q, k, nv, 3000, forced, n_last, 1e7, 1.0, return_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(vs2, vs)
+    for h in range(Hq):
+        assert vert[h].cpu().long().tolist() == O.top_with_forced(vs2[h].double().cpu(), nv, forced).tolist()
+        assert slash[h].cpu().long().tolist() == O.top_with_forced(ss2[h].double().cpu(), 3000, forced).tolist()
+    rows = torch.arange(S - n_last, S)
+    _, _, ref_vs, ref_ss = O.vs_estimate(q[0, :, rows].cpu(), rows, k[0].cpu(), 1e7, nv, 3000, forced, 1.0)
+    ev = (vs2.double().cpu() - ref_vs).abs().max().item()
+    es = (ss2.double().cpu() - ref_ss).abs().max().item()
+    say(f"  score err vertical={ev:.3e} slash={es:.3e}; budget {nv}")
+    assert ev <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_vs_estimate_finds_planted_pattern_and_drives_sparse_prefill():
     """Keys planted along a column and along a diagonal are found at a
     16K-token sequence, and the lists drive the sparse prefill."""
