@@ -124,13 +124,18 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
     const int kt0 = split * a.tiles_per_split;
     const int kt1 = min(kt0 + a.tiles_per_split, a.n_tiles);
     float m_run = -INFINITY, l_run = 0.f;
-    for (int kt = kt0; kt < kt1; ++kt) {
+    // the next tile's key fragments load while the current tile is scored
+    auto load_tile = [&](int kt, vec (&dst)[2 * NU]) __attribute__((always_inline)) {
         const vec *k = (const vec *)(kbase + (int64_t)kt * TILE_BYTES);
+#pragma unroll
+        for (int i = 0; i < 2 * NU; ++i) dst[i] = k[i * 64 + lane];
+    };
+    auto score_tile = [&](int kt, const vec (&kf)[2 * NU]) __attribute__((always_inline)) {
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) F::mma(k[(kb * NU + u) * 64 + lane], qf[u], s[kb]);
+            for (int kb = 0; kb < 2; ++kb) F::mma(kf[kb * NU + u], qf[u], s[kb]);
         // S^T: value v of block kb is key j0 + 32 kb + 8 (v / 4) + 4 g + v % 4 of row `row`
         const int64_t j0 = (int64_t)kt * kTile;
         float mx = -INFINITY;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
                 mx = fmaxf(mx, s[kb][v]);
             }
         mx = fmaxf(mx, est_swap32(mx));
-        if (mx == -INFINITY) continue;                 // no key of this tile is visible to the row
+        if (mx == -INFINITY) return;                   // no key of this tile is visible to the row
         const float m_new = fmaxf(m_run, mx);
         float sum = 0.f;
 #pragma unroll
@@ -152,6 +157,15 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
             for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(s[kb][v] - m_new);
         l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + sum;
         m_run = m_new;
+    };
+    vec ka[2 * NU], kn[2 * NU];
+    if (kt0 < kt1) load_tile(kt0, ka);
+    for (int kt = kt0; kt < kt1; kt += 2) {
+        if (kt + 1 < kt1) load_tile(kt + 1, kn);
+        score_tile(kt, ka);
+        if (kt + 1 >= kt1) break;
+        if (kt + 2 < kt1) load_tile(kt + 2, ka);
+        score_tile(kt + 1, kn);
     }
     const float l_tot = l_run + est_swap32(l_run);
     if (g == 0) {
@@ -215,33 +229,42 @@ __global__ __launch_bounds__(64) void est_sums_kernel(EstArgs a) {
     const int kt1 = min(kt0 + a.tiles_per_split, a.n_tiles);
     float *vs = a.vscore + (int64_t)h * a.S;
     float *ss = a.sscore + (int64_t)h * a.S;
-    for (int kt = kt0; kt < kt1; ++kt) {
+    // one 32-key half of key fragments is always in flight: the second half
+    // of the tile while the first is summed, the next tile's first half
+    // while the second is
+    auto load_half = [&](int kt, int kb, vec (&dst)[NU]) __attribute__((always_inline)) {
         const vec *k = (const vec *)(kbase + (int64_t)kt * TILE_BYTES);
-        const int64_t j0 = (int64_t)kt * kTile;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            vec kfr[NU];
+        for (int u = 0; u < NU; ++u) dst[u] = k[(kb * NU + u) * 64 + lane];
+    };
+    auto sum_half = [&](int64_t j0, int kb, const vec (&kfr)[NU]) __attribute__((always_inline)) {
+        const int64_t j = j0 + kBlk * kb + x;          // this lane's key
+        float col = 0.f;
 #pragma unroll
-            for (int u = 0; u < NU; ++u) kfr[u] = k[(kb * NU + u) * 64 + lane];
-            const int64_t j = j0 + kBlk * kb + x;      // this lane's key
-            float col = 0.f;
+        for (int rb = 0; rb < 2; ++rb) {
+            f32x16 acc = {};
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                f32x16 acc = {};
+            for (int u = 0; u < NU; ++u) F::mma(qf[rb][u], kfr[u], acc);
 #pragma unroll
-                for (int u = 0; u < NU; ++u) F::mma(qf[rb][u], kfr[u], acc);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int rl = kBlk * rb + 8 * (v / 4) + 4 * g + (v % 4);
-                    const int64_t row = (int64_t)a.r0 + rl;
-                    const float p = j <= row ? __builtin_amdgcn_exp2f(acc[v] - rm[rb][v]) * ril[rb][v] : 0.f;
-                    col += p;
-                    P[rl * LD + kBlk * kb + x] = p;
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int rl = kBlk * rb + 8 * (v / 4) + 4 * g + (v % 4);
+                const int64_t row = (int64_t)a.r0 + rl;
+                const float p = j <= row ? __builtin_amdgcn_exp2f(acc[v] - rm[rb][v]) * ril[rb][v] : 0.f;
+                col += p;
+                P[rl * LD + kBlk * kb + x] = p;
             }
-            col += est_swap32(col);
-            if (g == 0 && j < a.S) vs[j] = col;
         }
+        col += est_swap32(col);
+        if (g == 0 && j < a.S) vs[j] = col;
+    };
+    vec k0[NU], k1[NU];
+    if (kt0 < kt1) load_half(kt0, 0, k0);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int64_t j0 = (int64_t)kt * kTile;
+        load_half(kt, 1, k1);
+        sum_half(j0, 0, k0);
+        if (kt + 1 < kt1) load_half(kt + 1, 0, k0);
+        sum_half(j0, 1, k1);
         __syncthreads();
         // diagonal sums of the tile (a = row - r0, b = key - j0): lane t reads
         // P[r][(r - t) mod 64] for every r, which is diagonal a - b = t for
@@ -325,6 +348,16 @@ __device__ __forceinline__ void hist_add(unsigned *hist, unsigned bin, bool vali
     if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
+// scores b0 + e * kTopkThreads + tid, e < kTopkPer (0 past the end): coalesced
+__device__ __forceinline__ void load_step(const unsigned *bits, int64_t n, int64_t b0, int tid,
+                                          unsigned (&v)[kTopkPer]) {
+#pragma unroll
+    for (int e = 0; e < kTopkPer; ++e) {
+        const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
+        v[e] = i < n ? bits[i] : 0u;
+    }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
     __shared__ unsigned hist[256];
     __shared__ int wsum[kTopkThreads / 64];
@@ -350,18 +383,18 @@ __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
         __syncthreads();
+        // the next step's scores load while this step's are counted
+        unsigned v[kTopkPer], vn[kTopkPer];
+        load_step(bits, n, f, tid, v);
         for (int64_t b0 = f; b0 < n; b0 += kTopkStep) {
-            unsigned v[kTopkPer];
-#pragma unroll
-            for (int e = 0; e < kTopkPer; ++e) {
-                const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
-                v[e] = i < n ? bits[i] : 0u;
-            }
+            if (b0 + kTopkStep < n) load_step(bits, n, b0 + kTopkStep, tid, vn);
 #pragma unroll
             for (int e = 0; e < kTopkPer; ++e) {
                 const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
                 hist_add(hist, (v[e] >> shift) & 255u, i < n && (v[e] & pmask) == prefix);
             }
+#pragma unroll
+            for (int e = 0; e < kTopkPer; ++e) v[e] = vn[e];
         }
         __syncthreads();
         if (tid == 0) {
@@ -387,12 +420,12 @@ __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
     const int R = (int)remaining;
     int pos = f;
     int ties = 0;                                      // equal bits seen before this step
+    unsigned cv[kTopkPer], cn[kTopkPer];
+    load_step(bits, n, f, tid, cv);
     for (int64_t b0 = f; b0 < n && pos < budget; b0 += kTopkStep) {
 #pragma unroll
-        for (int e = 0; e < kTopkPer; ++e) {
-            const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
-            stage[e * kTopkThreads + tid] = i < n ? bits[i] : 0u;
-        }
+        for (int e = 0; e < kTopkPer; ++e) stage[e * kTopkThreads + tid] = cv[e];
+        if (b0 + kTopkStep < n) load_step(bits, n, b0 + kTopkStep, tid, cn);
         __syncthreads();
         unsigned w[kTopkPer];
         int gt = 0, eq = 0;
@@ -423,6 +456,8 @@ __global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
         const int tot_gt = total & 0xffff, tot_eq = total >> 16;
         pos += tot_gt + min(tot_eq, r_left);
         ties += tot_eq;
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) cv[e] = cn[e];
         __syncthreads();                               // stage is rewritten next step
     }
 }
