@@ -587,6 +587,80 @@ def test_fused_rotation_vertical_slash():
 
 
 # ---------------------------------------------------------------------------
+# batch > 1: each sequence of the batch against the oracle, and bit for bit
+# against its own single-sequence call
+# ---------------------------------------------------------------------------
+
+def _one(t, b):
+    return t[b:b + 1].contiguous()
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,D,S,C,W", [
+    ("bf16", 3, 4, 2, 64, 700, 128, 32),     # ragged tail, G = 2
+    ("f32", 2, 2, 1, 128, 300, 64, 64),      # fp32, W = C
+])
+def test_batched_prefill(dtype, B, Hq, Hkv, D, S, C, W):
+    say(f"[batched] dtype={dtype} B={B} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W}")
+    w = workloads.Workload("t", B, Hq, Hkv, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True)
+    q, k, v = synth.make_qkv(w, seed=61, device=DEV)
+    out, lse = _run(q, k, v, w)
+    ref, ref_lse = _oracle(q, k, v, np.arange(S), w)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL[dtype] and lerr <= (1e-4 if dtype == "f32" else 2e-2)
+    w1 = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, dtype, w.input_scale, True)
+    for b in range(B):
+        o1, l1 = _run(_one(q, b), _one(k, b), _one(v, b), w1)
+        assert torch.equal(o1[0], out[b]) and torch.equal(l1[0], lse[b])
+
+
+def test_batched_vertical_slash():
+    w = _wl("qwen14b_1m_vs", batch=2, seq=3000, chunk=1024, window=128, n_vertical=40, n_slash=60, n_q_heads=4,
+            n_kv_heads=2)
+    say(f"[batched vs] B=2 S={w.seq} C={w.chunk} W={w.window} nv=40 ns=60")
+    q, k, v = synth.make_qkv(w, seed=62, device=DEV)
+    vert, slash = _vs_case(w, seed=62)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    out, lse = _run(q, k, v, w, vertical=vd, slash=sd)
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, 400, seed=2)
+    ref, ref_lse = _oracle(q, k, v, rows, w, vertical=vert, slash=slash)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    err, lerr = _err(out[:, :, rows_t], ref), _err(lse[:, :, rows_t], ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    w1 = _wl("qwen14b_1m_vs", batch=1, seq=3000, chunk=1024, window=128, n_vertical=40, n_slash=60, n_q_heads=4,
+             n_kv_heads=2)
+    for b in range(2):
+        o1, l1 = _run(_one(q, b), _one(k, b), _one(v, b), w1, vertical=vd, slash=sd)
+        assert torch.equal(o1[0], out[b]) and torch.equal(l1[0], lse[b])
+
+
+def test_batched_chunked_and_fused_equal_whole():
+    w = workloads.Workload("t", 2, 4, 2, 128, 2500, 512, 64, "bf16", 0.5, True)
+    say(f"[batched chunked/fused] B=2 S={w.seq} C={w.chunk} W={w.window} block=768")
+    q, k, v = synth.make_qkv(w, seed=63, device=DEV)
+    full, full_lse = _run(q, k, v, w)
+    out, lse = api.prefill_chunked(q, k, v, w.chunk, w.window, 768, w.rope_base, w.yarn_scale, return_lse=True)
+    fo, fl = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, return_lse=True, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full) and torch.equal(lse, full_lse)
+    assert torch.equal(fo, full) and torch.equal(fl, full_lse)
+
+
+def test_batched_decode():
+    w = workloads.Workload("t", 2, 8, 2, 128, 1200, 512, 64, "bf16", 0.5, True)
+    prompt, steps = 1100, 20
+    say(f"[batched decode] B=2 S={w.seq} C={w.chunk} W={w.window} prompt={prompt} steps={steps}")
+    q, k, v = synth.make_qkv(w, seed=64, device=DEV)
+    out, lse = _decode_run(q, k, v, w, prompt, steps)
+    rows = np.arange(prompt, prompt + steps)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+
+
+# ---------------------------------------------------------------------------
 # online vertical-slash estimation (continuous positions)
 # ---------------------------------------------------------------------------
 
