@@ -661,6 +661,80 @@ def test_batched_decode():
 
 
 # ---------------------------------------------------------------------------
+# HIP graph capture: the library records only kernel launches on the
+# caller's stream (no allocation, memset or synchronization), so a call can
+# be captured and replayed
+# ---------------------------------------------------------------------------
+
+def _replays_match(capture, outputs, refs, replays=3):
+    """Capture `capture()` in a graph after one eager warm-up on a side
+    stream, then replay it several times with eager work in between; every
+    replay must reproduce `refs` bit for bit."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capture()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture()
+    for r in range(replays):
+        for o in outputs:
+            o.fill_(float("nan"))                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outputs, refs):
+            assert torch.equal(o, ref), f"replay {r}"
+
+
+def test_graph_capture_prefill_and_decode():
+    w = workloads.Workload("t", 1, 4, 2, 128, 3000, 1024, 128, "bf16", 0.5, True)
+    say(f"[graph] S={w.seq} C={w.chunk} W={w.window}: dense, vertical-slash, decode")
+    q, k, v = synth.make_qkv(w, seed=71, device=DEV)
+    shape = api.shape_of(q, k)
+    S, C, W = w.seq, w.chunk, w.window
+    # dense prefill
+    ref_out, ref_lse = _run(q, k, v, w)
+    nbytes = api.dca_workspace_size(S, C, W, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    _replays_match(lambda: api.dca_prefill(q, k, v, out, lse, S, C, W, w.rope_base, w.yarn_scale, None, shape, ws,
+                                           nbytes), [out, lse], [ref_out, ref_lse])
+    # vertical-slash prefill
+    wv = _wl("qwen14b_1m_vs", seq=S, chunk=C, window=W, n_vertical=40, n_slash=60, n_q_heads=4, n_kv_heads=2)
+    vert, slash = _vs_case(wv, seed=71)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    ref_vo, ref_vl = _run(q, k, v, w, vertical=vd, slash=sd)
+    mask = api.make_mask(vd, sd)
+    vbytes = api.dca_workspace_size(S, C, W, shape, mask)
+    vws = api.alloc_workspace(vbytes, DEV)
+    _replays_match(lambda: api.dca_prefill(q, k, v, out, lse, S, C, W, w.rope_base, w.yarn_scale, mask, shape, vws,
+                                           vbytes), [out, lse], [ref_vo, ref_vl])
+    # one decode step after a 2900-row prompt (it rewrites the same cache slot)
+    prompt = 2900
+    dbytes = api.dca_chunk_workspace_size(S, prompt, C, W, shape)
+    dws = api.alloc_workspace(dbytes, DEV)
+    po = torch.empty_like(q[:, :, :prompt])
+    api.dca_prefill_chunk(q[:, :, :prompt].contiguous(), k[:, :, :prompt].contiguous(),
+                          v[:, :, :prompt].contiguous(), po, None, 0, prompt, S, C, W, w.rope_base, w.yarn_scale,
+                          None, shape, dws, dbytes)
+    qt, kt, vt = (t[:, :, prompt].contiguous() for t in (q, k, v))
+    do = torch.empty_like(qt)
+    dl = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+
+    def dec():
+        api.dca_decode(qt, kt, vt, do, dl, prompt, S, C, W, w.rope_base, w.yarn_scale, shape, dws, dbytes)
+
+    dec()
+    torch.cuda.synchronize()
+    ref_do, ref_dl = do.clone(), dl.clone()
+    _replays_match(dec, [do, dl], [ref_do, ref_dl])
+
+
+# ---------------------------------------------------------------------------
 # online vertical-slash estimation (continuous positions)
 # ---------------------------------------------------------------------------
 
