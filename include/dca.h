@@ -36,6 +36,8 @@
  *   - Device entry points enqueue on `stream` (a hipStream_t; NULL = the
  *     null stream) and return without synchronizing. Results are valid
  *     after the stream is synchronized. Launch failures return DCA_E_DEVICE.
+ *     They enqueue kernel launches only (no allocation, memset, copy or
+ *     synchronization), so a call may be captured into a HIP graph.
  *   - Pointers marked "device" are caller-owned device memory; the library
  *     allocates and frees nothing.
  *   - Tensors are contiguous row-major; q, out: [batch, n_q_heads, seq,

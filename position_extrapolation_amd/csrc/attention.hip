@@ -147,7 +147,6 @@ struct TileIter {
 };
 
 // Per-wave constants of the tile loop.
-// Per-wave constants of the tile loop.
 struct WaveCtx {
     int lane, x, gsel, wave, r0, tb_succ, tb_intra, wave_qt;
     bool active_rows;

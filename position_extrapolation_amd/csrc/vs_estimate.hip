@@ -492,7 +492,8 @@ static int launch_est_t(const Problem &p, int n_last, const void *q, const void 
         e.n_split = (e.n_tiles + e.tiles_per_split - 1) / e.tiles_per_split;
         e.n_sets = (int32_t)(p.Hkv * e.n_split);
     };
-    // many more waves than fit at once, so that no pass ends on a thin last round
+    // many more waves than fit at once, so that no pass ends with a thinly
+    // occupied last batch of workgroups
     EstArgs ar = a;
     set_splits(ar, kEstRowstatWaves, 2 * (int)p.G);
     set_splits(a, kEstSumsWaves, (int)p.G);
