@@ -343,6 +343,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
     st.mref = 0.f;
     st.l_run = 0.f;
+    f32x16 c0 = {};                  // start of the score accumulators: -mref (0 before the first tile)
 
     // ---- tile window and prologue ---------------------------------------------
     // A step handles TPS key tiles between two barriers. LDS holds a ring of NS
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
                 if (i > 0) load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
                 const char *cur = lds + ((n * TPS + i) % NS) * 2 * TILE_BYTES;
                 f32x16 s[2];
-                tile_scores<T, D, true>(c.lane, st, cur, s);
+                tile_scores_from<T, D, true>(c.lane, st, c0, cur, s);
                 if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
                 VFrags<T, D> vf;
                 load_v<T, D>(c.lane, cur + TILE_BYTES, vf);
@@ -399,6 +400,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
                 if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
                     raise_ref<T, D>(st, s);
                     psum = tile_p<T>(s, p);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) c0[v] = -st.mref;
                 }
                 st.l_run += psum;
                 __builtin_amdgcn_sched_barrier(0);

@@ -27,6 +27,10 @@ struct Frag<__bf16> {
     __device__ static inline void mma(const vec &a, const vec &b, f32x16 &c) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // c0 + A * B as a new value (c0 stays live)
+    __device__ static inline f32x16 mma_from(const vec &a, const vec &b, const f32x16 &c0) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    }
     // acc + sum of the 8 elements (two-element dot products with ones)
     __device__ static inline float sum_into(const vec &v, float acc) {
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -52,6 +56,12 @@ struct Frag<float> {
     __device__ static inline void mma(const vec &a, const vec &b, f32x16 &c) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], c, 0, 0, 0);
+    }
+    __device__ static inline f32x16 mma_from(const vec &a, const vec &b, const f32x16 &c0) {
+        f32x16 c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c0, 0, 0, 0);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], c, 0, 0, 0);
+        return c;
     }
     __device__ static inline float sum_into(const vec &v, float acc) { return acc + ((v[0] + v[1]) + (v[2] + v[3])); }
 };

@@ -79,6 +79,35 @@ __device__ __forceinline__ void tile_scores(int lane, const WaveState<T, D> &st,
     }
 }
 
+// The same with the accumulators started from c0, a tuple the caller keeps
+// equal to the start value (-mref, or 0 before the first tile): the first
+// matrix-core op of each accumulator reads c0 and writes a fresh result, so
+// no per-tile initialisation runs on the vector ALU.
+template <typename T, int D, bool LDS_SCHED>
+__device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D> &st, const f32x16 &c0,
+                                                 const char *__restrict__ kl, f32x16 (&s)[2]) {
+    using F = Frag<T>;
+    using vec = typename F::vec;
+    constexpr int NU = WaveState<T, D>::NU;
+    const vec *k = (const vec *)kl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = F::mma_from(k[(kb * NU) * 64 + lane], st.qfrag[0], c0);
+#pragma unroll
+    for (int u = 1; u < NU; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) F::mma(k[(kb * NU + u) * 64 + lane], st.qfrag[u], s[kb]);
+    if constexpr (LDS_SCHED && sizeof(T) == 2) {
+        constexpr int N = 2 * NU, AHEAD = N < 4 ? N : 4;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < N - AHEAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
+    }
+}
+
 // P = 2^s rounded to the operand type, in PV fragment order; returns this
 // lane's sum of the rounded P.
 template <typename T>
