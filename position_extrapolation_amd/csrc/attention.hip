@@ -259,9 +259,14 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, Wave
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Waves per SIMD the register budget is sized for: two (256 registers per
+// wave), except fp32 with d = 128, whose V fragments alone take 128 registers
+// per lane: one (512), so that nothing spills.
+template <typename T, int D>
+constexpr int kMinWavesPerSimd = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+
 template <typename T, int D, int NW, int NS, int TPS, bool FUSED>
-// second bound: at least two waves per SIMD (256 registers per wave)
-__global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attention_kernel(AttnArgs a) {
     using F = Frag<T>;
     using vec = typename F::vec;
     constexpr int E = F::E;
@@ -343,7 +348,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
     st.mref = 0.f;
     st.l_run = 0.f;
-    f32x16 c0 = {};                  // start of the score accumulators: -mref (0 before the first tile)
+    // start of the score accumulators, -mref (0 before the first tile), kept
+    // in registers where they fit: bf16 with materialized query variants
+    constexpr bool C0 = sizeof(T) == 2 && !FUSED;
+    f32x16 c0 = {};
 
     // ---- tile window and prologue ---------------------------------------------
     // A step handles TPS key tiles between two barriers. LDS holds a ring of NS
@@ -389,7 +397,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
                 if (i > 0) load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
                 const char *cur = lds + ((n * TPS + i) % NS) * 2 * TILE_BYTES;
                 f32x16 s[2];
-                tile_scores_from<T, D, true>(c.lane, st, c0, cur, s);
+                if constexpr (C0)
+                    tile_scores_from<T, D, true>(c.lane, st, c0, cur, s);
+                else
+                    tile_scores<T, D, true>(c.lane, st, cur, s);
                 if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
                 VFrags<T, D> vf;
                 load_v<T, D>(c.lane, cur + TILE_BYTES, vf);
@@ -400,8 +411,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dca_attention_kernel(AttnArgs a) {
                 if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
                     raise_ref<T, D>(st, s);
                     psum = tile_p<T>(s, p);
+                    if constexpr (C0) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) c0[v] = -st.mref;
+                        for (int v = 0; v < 16; ++v) c0[v] = -st.mref;
+                    }
                 }
                 st.l_run += psum;
                 __builtin_amdgcn_sched_barrier(0);
