@@ -22,7 +22,8 @@
 // Vertical-slash mode [mizuki, MInference sections]: the workgroup visits
 // the union of the active key tiles of its 64-row query tiles, merging each
 // head's sorted tile list VT and distance list D on the fly; a wave skips
-// tiles inactive for its own query tile.
+// tiles inactive for its own query tile. Its scattered tiles come through
+// separate LDS rings (SPLIT): K two tiles ahead, V one.
 //
 // Grid order: heaviest row tiles first; the work list is cut into per-XCD
 // streams so that the workgroups resident on one XCD (workgroup i lands on
@@ -265,7 +266,7 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, Wave
 template <typename T, int D>
 constexpr int kMinWavesPerSimd = (sizeof(T) == 4 && D == 128) ? 1 : 2;
 
-template <typename T, int D, int NW, int NS, int TPS, bool FUSED>
+template <typename T, int D, int NW, int NS, int TPS, bool FUSED, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attention_kernel(AttnArgs a) {
     using F = Frag<T>;
     using vec = typename F::vec;
@@ -353,6 +354,66 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     constexpr bool C0 = sizeof(T) == 2 && !FUSED;
     f32x16 c0 = {};
 
+    // The per-tile work (QK, mask, softmax step, PV) is written out in both
+    // loops below: moved into a shared function or lambda, it changes the
+    // register allocation and spills.
+    if constexpr (SPLIT) {
+        // separate rings: K in 3 slots (two tiles ahead), V in 2 (one ahead).
+        // Per step: V(n+1), then K(n+2); at the next step's top every load but
+        // that K has landed (loads complete in issue order).
+        constexpr int KL = TILE_BYTES / 1024 / NW;       // loads per wave and tile
+        const uint32_t vbase_lds = lds_base + 3u * TILE_BYTES;
+        TileIter<NT> it;
+        it.init(a, h, i0, S, last_row / kTile);
+        int t[3];
+        unsigned m[3] = {0, 0, 0};
+        t[0] = it.next(m[0]);
+        t[1] = t[0] >= 0 ? it.next(m[1]) : -1;
+        t[2] = t[1] >= 0 ? it.next(m[2]) : -1;
+        if (t[0] >= 0) {
+            dma_tile<T, D, NW>(c, c.kbytes, t[0], lds_base);
+            dma_tile<T, D, NW>(c, c.vbytes, t[0], vbase_lds);
+        }
+        if (t[1] >= 0) dma_tile<T, D, NW>(c, c.kbytes, t[1], lds_base + 1u * TILE_BYTES);
+        for (int n = 0; t[0] >= 0; ++n) {
+            if (t[1] >= 0) wait_vmcnt<KL>(); else __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                 // K(n), V(n) landed; V slot (n+1)%2 and K slot (n+2)%3 are free
+            if (t[1] >= 0) dma_tile<T, D, NW>(c, c.vbytes, t[1], vbase_lds + (uint32_t)((n + 1) & 1) * TILE_BYTES);
+            if (t[2] >= 0) dma_tile<T, D, NW>(c, c.kbytes, t[2], lds_base + (uint32_t)((n + 2) % 3) * TILE_BYTES);
+            const int kt = t[0];
+            if (active(c, kt, m[0])) {
+                load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
+                const char *kcur = lds + (n % 3) * TILE_BYTES;
+                const char *vcur = lds + 3 * TILE_BYTES + (n & 1) * TILE_BYTES;
+                f32x16 s[2];
+                if constexpr (C0)
+                    tile_scores_from<T, D, true>(c.lane, st, c0, kcur, s);
+                else
+                    tile_scores<T, D, true>(c.lane, st, kcur, s);
+                if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
+                VFrags<T, D> vf;
+                load_v<T, D>(c.lane, vcur, vf);
+                __builtin_amdgcn_sched_barrier(0);
+                vec p[2][NUV];
+                float psum = tile_p<T>(s, p);
+                const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
+                if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
+                    raise_ref<T, D>(st, s);
+                    psum = tile_p<T>(s, p);
+                    if constexpr (C0) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) c0[v] = -st.mref;
+                    }
+                }
+                st.l_run += psum;
+                __builtin_amdgcn_sched_barrier(0);
+                tile_pv<T, D>(st, vf, p);
+            }
+            t[0] = t[1]; m[0] = m[1];
+            t[1] = t[2]; m[1] = m[2];
+            t[2] = t[1] >= 0 ? it.next(m[2]) : -1;
+        }
+    } else {
     // ---- tile window and prologue ---------------------------------------------
     // A step handles TPS key tiles between two barriers. LDS holds a ring of NS
     // slots of [K tile | V tile]; tile j (in visiting order) lives in slot
@@ -430,6 +491,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
         for (int i = NS - TPS; i < NS; ++i) t[i] = t[i - 1] >= 0 ? it.next(m[i]) : -1;
     }
 
+    }
     // ---- epilogue -----------------------------------------------------------
     const int row = c.r0 + c.x;
     if (!c.active_rows || row >= S) return;
@@ -450,7 +512,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     }
 }
 
-template <typename T, int D, int NW, int NS, int TPS>
+template <typename T, int D, int NW, int NS, int TPS, bool SPLIT = false>
 static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
     constexpr int BM = kBlk * NW;
     AttnArgs a = a0;
@@ -469,9 +531,10 @@ static int launch_attn_t(const Problem &p, const AttnArgs &a0, void *stream) {
         a.per_xcd = (int32_t)(per_stream * a.M * a.G);
     }
     const int64_t grid = (int64_t)a.per_xcd * kXcds;
-    const int lds_bytes = NS * 2 * (2 * kBlk * D * (int)sizeof(T));   // NS slots of [K tile | V tile]
-    auto kern = a.q_nat != nullptr ? dca_attention_kernel<T, D, NW, NS, TPS, true>
-                                   : dca_attention_kernel<T, D, NW, NS, TPS, false>;
+    // NS slots of [K tile | V tile], or 3 K slots and 2 V slots (SPLIT)
+    const int lds_bytes = (SPLIT ? 5 : 2 * NS) * (2 * kBlk * D * (int)sizeof(T));
+    auto kern = a.q_nat != nullptr ? dca_attention_kernel<T, D, NW, NS, TPS, true, SPLIT>
+                                   : dca_attention_kernel<T, D, NW, NS, TPS, false, SPLIT>;
     if (lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  lds_bytes);
@@ -513,7 +576,7 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
     // Sparse: 128-row workgroups, two per CU. A workgroup visits the union of
     // its query tiles' active key tiles, so fewer query tiles per workgroup
     // leave fewer waves idle on each visited tile.
-    if (p.dtype == DCA_BF16 && p.sparse && p.D == 128) return launch_attn_t<__bf16, 128, 4, 2, 1>(p, a, stream);
+    if (p.dtype == DCA_BF16 && p.sparse && p.D == 128) return launch_attn_t<__bf16, 128, 4, 2, 1, true>(p, a, stream);
     if (p.dtype == DCA_BF16)
         return p.D == 128 ? launch_attn_t<__bf16, 128, 8, 4, 2>(p, a, stream)
                           : launch_attn_t<__bf16, 64, 8, 4, 2>(p, a, stream);
