@@ -15,8 +15,9 @@ attention kernel against the bf16 dense MFMA peak; `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload; `extra` holds the other
 measured workloads: 128K dense, 1M vertical-slash, the 1M sequence as a
 chunked prefill in 32,768-row blocks, decode at a 1M context, the 1M path
-with the query rotation fused into the attention kernel, and the online
-vertical-slash estimate at 1M.
+with the query rotation fused into the attention kernel, the online
+vertical-slash estimate at 1M, and the online flow end to end (estimate,
+then the sparse prefill with the estimated mask) beside the dense step.
 """
 
 from __future__ import annotations
@@ -280,6 +281,57 @@ def measure_estimate(name, device, n_vertical=1000, n_slash=2000, forced=64, n_l
     return res
 
 
+def measure_online_vs(name, device, dense_step_ms=None, n_vertical=1000, n_slash=2000, forced=64, n_last=64):
+    """The online vertical-slash flow on the workload's shape [mizuki,
+    MInference sections]: each head's columns and offsets estimated from the
+    last 64 rows under continuous positions (dca_vs_estimate), then the DCA
+    prefill with that mask (dca_prefill: remap, tile index, sparse attention),
+    timed as one step. The work is the active-tile pairs of the estimated
+    mask; the dense prefill step of the same run is the comparison."""
+    w = workloads.get(name)
+    log(f"[bench] generating inputs for {name} online vertical-slash")
+    q, k, v = synth.make_qkv(w, seed=0, device=device)
+    shape = api.shape_of(q, k)
+    eb = api.dca_vs_estimate_workspace_size(w.seq, shape)
+    ews = api.alloc_workspace(eb, device)
+    vert = torch.empty((w.n_q_heads, n_vertical), dtype=torch.int32, device=device)
+    slash = torch.empty((w.n_q_heads, n_slash), dtype=torch.int32, device=device)
+    mask = api.make_mask(vert, slash)
+    pb = api.dca_workspace_size(w.seq, w.chunk, w.window, shape, mask)
+    pws = api.alloc_workspace(pb, device)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.dca_vs_estimate(q, k, w.seq, n_last, w.rope_base, w.yarn_scale, n_vertical, n_slash, forced, shape,
+                            vert, slash, None, None, ews, eb)
+        if ev is not None:
+            ev[1].record()
+        api.dca_prefill(q, k, v, out, None, w.seq, w.chunk, w.window, w.rope_base, w.yarn_scale, mask, shape,
+                        pws, pb)
+        if ev is not None:
+            ev[2].record()
+
+    step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    step(ev)
+    torch.cuda.synchronize()
+    est_ms, pre_ms = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    ms = est_ms + pre_ms
+    flops = 4.0 * w.head_dim * vs_active_pairs(w, vert.cpu().numpy(), slash.cpu().numpy())
+    res = {"workload": f"{name}_online_vs", "n_vertical": n_vertical, "n_slash": n_slash, "ms_per_step": ms,
+           "estimate_ms": est_ms, "prefill_ms": pre_ms, "active_fraction": flops / w.dense_flops(),
+           "tflops": flops / (ms * 1e-3) / 1e12, "dense_equiv_tflops": w.dense_flops() / (ms * 1e-3) / 1e12}
+    if dense_step_ms is not None:
+        res["speedup_vs_dense_step"] = dense_step_ms / ms
+    log(f"[bench] {json.dumps(res)}")
+    del q, k, v, ews, pws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_decode(name, steps, device):
     """DCA decode of the last `steps` tokens of the workload's sequence, one
     dca_decode call each, against the key/value cache of everything before
@@ -385,8 +437,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen14b_1m")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra workloads (128K, vertical-slash, chunked, decode, fused, estimate)")
-    ap.add_argument("--only", choices=["decode", "chunked", "fused", "estimate"],
+                    help="skip the extra workloads (128K, vertical-slash, chunked, decode, fused, estimate, "
+                         "online vertical-slash)")
+    ap.add_argument("--only", choices=["decode", "chunked", "fused", "estimate", "online"],
                     help="run just this 1M measurement and print its JSON (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16)
@@ -409,7 +462,8 @@ def main():
         run = {"decode": lambda: measure_decode("qwen14b_1m", 64, dev),
                "chunked": lambda: measure_chunked("qwen14b_1m", 32768, 1, 0, dev),
                "fused": lambda: measure_fused("qwen14b_1m", dev),
-               "estimate": lambda: measure_estimate("qwen14b_1m", dev)}[args.only]
+               "estimate": lambda: measure_estimate("qwen14b_1m", dev),
+               "online": lambda: measure_online_vs("qwen14b_1m", dev)}[args.only]
         print(json.dumps(run()), flush=True)
         return
     api.lib()
@@ -425,6 +479,8 @@ def main():
         extra.append(measure_decode("qwen14b_1m", 64, dev))
         extra.append(measure_fused("qwen14b_1m", dev))
         extra.append(measure_estimate("qwen14b_1m", dev))
+        extra.append(measure_online_vs("qwen14b_1m", dev,
+                                       main_res["ms_per_step"] if w.name == "qwen14b_1m" else None))
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = main_res["attention_tflops"]
