@@ -216,41 +216,54 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void decode_attn_kernel
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 1024;
 
+// block-wide max / sum of one value per thread: a wave reduction, then one
+// pass over the 16 wave results
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float *wred) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float y = __shfl_xor(x, off, 64);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    if (lane == 0) wred[wave] = x;
+    __syncthreads();
+    float r = wred[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) r = MAX ? fmaxf(r, wred[w]) : r + wred[w];
+    __syncthreads();                             // wred is reused by the next reduction
+    return r;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
     constexpr int RPT = kCombineThreads / D;     // threads sharing one output element
     static_assert(kMaxSplits <= kCombineThreads, "one thread per split for the reductions");
     __shared__ float wgt[kMaxSplits];            // 2^(m_s - M), 0 for empty splits
     __shared__ float red[kCombineThreads];
+    __shared__ float wred[kCombineThreads / 64];
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
     const float *part = a.part + bh * kMaxSplits * (D + 2);
     const bool live = t < a.n_split && part[t * (D + 2) + D + 1] > 0.f;
     const float m = live ? part[t * (D + 2) + D] : -INFINITY;
-    // M = max over the live splits
-    red[t] = m;
-    __syncthreads();
-    for (int w = kCombineThreads / 2; w > 0; w /= 2) {
-        if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-        __syncthreads();
-    }
-    const float mx = red[0];
-    __syncthreads();
+    const float mx = block_reduce<true>(m, wred);                   // M over the live splits
     const float wt = live ? __builtin_amdgcn_exp2f(m - mx) : 0.f;
     if (t < kMaxSplits) wgt[t] = wt;
-    red[t] = live ? wt * part[t * (D + 2) + D + 1] : 0.f;
-    __syncthreads();
-    for (int w = kCombineThreads / 2; w > 0; w /= 2) {
-        if (t < w) red[t] += red[t + w];
-        __syncthreads();
-    }
-    const float den = red[0];
-    __syncthreads();
-    // O[d] = sum_s w_s O_s[d] / den: thread t sums every RPT-th split of element t % D
+    const float den = block_reduce<false>(live ? wt * part[t * (D + 2) + D + 1] : 0.f, wred);   // also orders wgt
+    // O[d] = sum_s w_s O_s[d] / den: thread t sums every RPT-th split of
+    // element t % D, four independent partial sums so the loads overlap
     const int d = t % D, r = t / D;
-    float num = 0.f;
-    for (int s = r; s < a.n_split; s += RPT) num += wgt[s] * part[s * (D + 2) + d];
-    red[t] = num;
+    float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f;
+    int s = r;
+    for (; s + 3 * RPT < a.n_split; s += 4 * RPT) {
+        n0 += wgt[s] * part[s * (D + 2) + d];
+        n1 += wgt[s + RPT] * part[(s + RPT) * (D + 2) + d];
+        n2 += wgt[s + 2 * RPT] * part[(s + 2 * RPT) * (D + 2) + d];
+        n3 += wgt[s + 3 * RPT] * part[(s + 3 * RPT) * (D + 2) + d];
+    }
+    for (; s < a.n_split; s += RPT) n0 += wgt[s] * part[s * (D + 2) + d];
+    red[t] = (n0 + n1) + (n2 + n3);
     __syncthreads();
     for (int w = RPT / 2; w > 0; w /= 2) {
         if (r < w) red[t] += red[t + w * D];
