@@ -118,6 +118,8 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
     const int h = kvh * a.G + member / 2, rb = member % 2;
     const int lane = threadIdx.x, x = lane % 32, g = lane / 32;
     const int64_t row = (int64_t)a.r0 + kBlk * rb + x;
+    const int64_t row_lo = (int64_t)a.r0 + kBlk * rb;          // the wave's first row
+    const bool rows_in = row_lo + kBlk - 1 < a.S;               // all 32 rows inside the sequence
     vec qf[NU];
     est_load_q<T, D>(a, h, rb, lane, qf);
     const char *kbase = (const char *)a.kf + (int64_t)kvh * a.nblk_kv * BLK_ELEMS * (int64_t)sizeof(T);
@@ -139,14 +141,21 @@ __global__ __launch_bounds__(64) void est_rowstat_kernel(EstArgs a) {
         // S^T: value v of block kb is key j0 + 32 kb + 8 (v / 4) + 4 g + v % 4 of row `row`
         const int64_t j0 = (int64_t)kt * kTile;
         float mx = -INFINITY;
+        if (j0 + kTile - 1 <= row_lo && rows_in) {      // every key visible to every row: no mask
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t j = j0 + kBlk * kb + 8 * (v / 4) + 4 * g + (v % 4);
-                if (j > row || row >= a.S) s[kb][v] = -INFINITY;
-                mx = fmaxf(mx, s[kb][v]);
-            }
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t j = j0 + kBlk * kb + 8 * (v / 4) + 4 * g + (v % 4);
+                    if (j > row || row >= a.S) s[kb][v] = -INFINITY;
+                    mx = fmaxf(mx, s[kb][v]);
+                }
+        }
         mx = fmaxf(mx, est_swap32(mx));
         if (mx == -INFINITY) return;                   // no key of this tile is visible to the row
         const float m_new = fmaxf(m_run, mx);
