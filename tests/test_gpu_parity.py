@@ -399,6 +399,30 @@ def test_vs_parity(S, C, W, nv, ns):
     assert err <= 0.1 * dd
 
 
+@pytest.mark.parametrize("dtype,D,S,C,W,nv,ns", [
+    ("bf16", 64, 2000, 512, 64, 12, 20),     # the d = 64 kernel instance
+    ("f32", 64, 1500, 256, 32, 10, 16),      # fp32 instances, all rows
+    ("f32", 128, 900, 128, 128, 8, 12),
+])
+def test_vs_parity_other_instances(dtype, D, S, C, W, nv, ns):
+    """Vertical-slash parity for the kernel instances other than bf16 d = 128
+    (which the cases above cover): all rows against the oracle."""
+    say(f"[vs parity] dtype={dtype} D={D} S={S} C={C} W={W} nv={nv} ns={ns}")
+    w = workloads.Workload("t", 1, 4, 2, D, S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0, True,
+                           n_vertical=nv, n_slash=ns)
+    q, k, v = synth.make_qkv(w, seed=81, device=DEV)
+    vert, slash = _vs_case(w, seed=81)
+    out, lse = _run(q, k, v, w, vertical=vert.to(DEV), slash=slash.to(DEV))
+    rows = np.arange(S)
+    ref, ref_lse = _oracle(q, k, v, rows, w, vertical=vert, slash=slash)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    dense, _ = _oracle(q, k, v, rows, w)
+    dd = (dense - ref).abs().max().item()
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}; dense-vs-sparse distance {dd:.3e}")
+    assert err <= TOL[dtype] and lerr <= (1e-4 if dtype == "f32" else 2e-2)
+    assert err <= 0.1 * dd
+
+
 # ---------------------------------------------------------------------------
 # chunked prefill: rows [q0, q0 + n) against keys [0, q0 + n), one workspace
 # ---------------------------------------------------------------------------
