@@ -432,6 +432,7 @@ def test_vs_parity_other_instances(dtype, D, S, C, W, nv, ns):
     ("bf16", 3, 1, 64, 1000, 128, 128, 64),       # 64-row blocks
     ("f32", 2, 1, 64, 2048, 512, 128, 320),       # fp32, blocks straddle chunk boundaries
     ("bf16", 2, 1, 128, 4096, 4096, 100, 4096),   # one block = the whole sequence
+    ("f32", 2, 1, 128, 700, 256, 64, 192),        # fp32, d = 128, ragged last block
 ])
 def test_chunked_equals_whole_prefill(dtype, Hq, Hkv, D, S, C, W, chunk):
     say(f"[chunked] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W} chunk={chunk}")
@@ -529,6 +530,7 @@ def _decode_run(q, k, v, w, prompt, steps):
     ("bf16", 5, 1, 128, 1100, 1024, 128, 1020),  # crosses the chunk boundary at 1024: intra -> new chunk
     ("f32", 4, 2, 64, 700, 128, 32, 600),        # fp32, d = 64, G = 2
     ("bf16", 7, 1, 64, 40, 64, 8, 0),            # no prompt: decode from pos 0 on a fresh workspace
+    ("f32", 4, 1, 128, 300, 128, 16, 250),       # fp32, d = 128, G = 4
 ])
 def test_decode_matches_oracle(dtype, Hq, Hkv, D, S, C, W, prompt):
     steps = min(S - prompt, 40)
@@ -772,6 +774,7 @@ def _est_case(dtype, Hq, Hkv, D, S, seed):
     ("f32", 3, 1, 64, 1000, 64, 50, 80, 16),
     ("bf16", 2, 1, 64, 333, 20, 40, 333, 8),       # fewer rows, every offset kept
     ("bf16", 5, 1, 128, 70, 64, 70, 10, 0),        # short sequence, no forced head
+    ("f32", 2, 1, 128, 900, 64, 60, 90, 16),       # fp32, d = 128
 ])
 def test_vs_estimate_matches_oracle(dtype, Hq, Hkv, D, S, n_last, nv, ns, forced):
     say(f"[vs estimate] dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} S={S} n_last={n_last} nv={nv} ns={ns} forced={forced}")
