@@ -240,6 +240,26 @@ def test_parity_sampled_rows_1m():
     _discrimination(q, k, v, rows, w, ref, out_rows)
 
 
+def test_parity_4m_tokens():
+    """A 4M-token sequence (2^22; one KV head, d = 64, C = 1M, W = 128K):
+    row, tile and byte offsets four times past the benchmark's largest shape.
+    The oracle on the forced boundary rows plus seeded rows, and the
+    wrong-mapping guard."""
+    w = workloads.Workload("t", 1, 2, 1, 64, 1 << 22, 1 << 20, 1 << 17, "bf16", 0.5, True)
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, 12, seed=4)
+    say(f"[parity 4M] S={w.seq} C={w.chunk} W={w.window}: {len(rows)} sampled rows x {w.n_q_heads} heads")
+    q, k, v = synth.make_qkv(w, seed=6, device=DEV)
+    out, lse = _run(q, k, v, w)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    out_rows, lse_rows = out[:, :, rows_t].clone(), lse[:, :, rows_t].clone()
+    del out, lse
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err, lerr = _err(out_rows, ref), _err(lse_rows, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    _discrimination(q, k, v, rows, w, ref, out_rows)
+
+
 def test_vs_parity_1m():
     """The 1M vertical-slash workload (1000 columns, 2000 offsets per head)
     on sampled rows."""
