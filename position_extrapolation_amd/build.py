@@ -61,7 +61,26 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
         raise RuntimeError("link of libdca.so failed")
     os.replace(tmp, LIB)
+    build_c_example(verbose)
     return LIB
+
+
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi_example")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """The plain C consumer the GPU tests run (tests/c_abi_example.c): gcc,
+    include/dca.h, libdca.so and the HIP runtime, nothing else."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include", f"-I{INCLUDE}",
+           C_EXAMPLE + ".c", "-o", C_EXAMPLE, f"-L{PKG}", "-ldca", f"-L{rocm}/lib", "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../position_extrapolation_amd", f"-Wl,-rpath,{rocm}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or r.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed on tests/c_abi_example.c")
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":

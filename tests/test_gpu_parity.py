@@ -781,6 +781,49 @@ def test_graph_capture_prefill_and_decode():
 
 
 # ---------------------------------------------------------------------------
+# a plain C consumer of the ABI (tests/c_abi_example.c, built by build())
+# ---------------------------------------------------------------------------
+
+def _splitmix_bf16(seed, n):
+    """The C example's inputs: splitmix64(seed + i) -> 24 bits in [-0.5, 0.5),
+    rounded to bf16 (nearest even) with the same integer steps."""
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + np.arange(n, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        z ^= z >> np.uint64(31)
+    f = (z >> np.uint64(40)).astype(np.float32) * np.float32(1.0 / 16777216.0) - np.float32(0.5)
+    u = f.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return torch.from_numpy(u.astype(np.uint16).view(np.int16).copy()).view(torch.bfloat16)
+
+
+def test_plain_c_consumer(tmp_path):
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_example")
+    if not os.path.exists(exe):
+        pytest.fail("tests/c_abi_example is missing: build it with __graft_entry__.build()")
+    B, Hq, Hkv, D, S, C, W = 1, 4, 2, 128, 3000, 1024, 128
+    say(f"[c consumer] {exe}: bf16 B={B} Hq={Hq} Hkv={Hkv} D={D} S={S} C={C} W={W}")
+    dst = str(tmp_path / "c_out.bin")
+    r = subprocess.run([exe, dst], capture_output=True, text=True, timeout=120)
+    say("  " + (r.stdout + r.stderr).strip())
+    assert r.returncode == 0
+    raw = open(dst, "rb").read()
+    nq, nl = B * Hq * S * D, B * Hq * S
+    c_out = torch.frombuffer(bytearray(raw[:2 * nq]), dtype=torch.bfloat16).view(B, Hq, S, D)
+    c_lse = torch.frombuffer(bytearray(raw[2 * nq:]), dtype=torch.float32).view(B, Hq, S)
+    q = _splitmix_bf16(1, nq).view(B, Hq, S, D).to(DEV)
+    k = _splitmix_bf16(2, B * Hkv * S * D).view(B, Hkv, S, D).to(DEV)
+    v = _splitmix_bf16(3, B * Hkv * S * D).view(B, Hkv, S, D).to(DEV)
+    yarn = float(np.float32(0.1 * math.log(S / C) + 1.0))
+    out, lse = api.prefill(q, k, v, C, W, 1e7, yarn, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), c_out) and torch.equal(lse.cpu(), c_lse)
+
+
+# ---------------------------------------------------------------------------
 # online vertical-slash estimation (continuous positions)
 # ---------------------------------------------------------------------------
 
