@@ -27,11 +27,11 @@
 //                        most two contributions (two key tiles), added
 //                        atomically to zero: the result does not depend on
 //                        their order;
-//   est_topk_kernel      per (head, list): radix select of the budget's
-//                        threshold on the scores' bits (histogram adds
-//                        grouped per wave and bin), then an index-ordered
-//                        compaction, 8192 scores per step, placed by one
-//                        block scan (ties to the smaller index).
+//   est_topk_*           per (head, list), 16 workgroups each: radix select
+//                        of the budget's threshold on the scores' bits (four
+//                        8-bit passes; histogram adds grouped per wave and
+//                        bin), then an index-ordered compaction placed by the
+//                        ranges' counts (ties to the smaller index).
 #include <hip/hip_runtime.h>
 
 #include "dca_internal.h"
@@ -295,15 +295,29 @@ __global__ __launch_bounds__(64) void est_sums_kernel(EstArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// top-k with forced head: grid (Hq, 2 lists) blocks of 1024 threads
+// top-k with forced head. Per (head, list) the candidates [f, n) are cut into
+// kTopkParts ranges, one workgroup each:
+//   est_topk_init    forced head, the take-everything cases, selection state
+//   est_topk_hist    per pass: the range's histogram of the next 8 bits of the
+//                    scores matching the prefix so far, added to the list's
+//                    global histogram
+//   est_topk_select  per pass: picks the bin holding the budget's edge, extends
+//                    the prefix, clears the histogram
+//   est_topk_count   per range: scores above the final prefix and equal to it
+//   est_topk_write   per range: its picks in index order, at the offset the
+//                    earlier ranges' counts give; ties go to the smaller index
 // ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkParts = 16;          // workgroups per (head, list)
+constexpr int kTopkBlock = 256;         // threads per workgroup
+constexpr int kTopkPer = 8;             // elements per thread and step
+constexpr int kTopkStep = kTopkBlock * kTopkPer;
 
 // inclusive prefix sum of one value per thread over the block; returns it and
 // the block total in *total
+template <int NT>
 __device__ int block_scan(int val, int *total, int *wsum) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    constexpr int NWAVES = kTopkThreads / 64;
+    constexpr int NWAVES = NT / 64;
     int x = val;
 #pragma unroll
     for (int d = 1; d < 64; d *= 2) {
@@ -334,10 +348,10 @@ struct TopkArgs {
     int32_t budget[2];
     int32_t forced;
     int64_t S;
+    unsigned *hist;                 // [Hq][2][256] histogram of the current pass
+    unsigned *state;                // [Hq][2][4]: prefix, prefix mask, equal bits still to take, active
+    int32_t *counts;                // [Hq][2][kTopkParts][2]: above, equal
 };
-
-constexpr int kTopkPer = 8;                          // elements per thread and step
-constexpr int kTopkStep = kTopkThreads * kTopkPer;
 
 // hist[bin] += 1 for the valid lanes. The scores crowd into a few bins, so
 // the lanes of a wave that share a bin add once, with their count (up to four
@@ -357,116 +371,174 @@ __device__ __forceinline__ void hist_add(unsigned *hist, unsigned bin, bool vali
     if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
-// scores b0 + e * kTopkThreads + tid, e < kTopkPer (0 past the end): coalesced
-__device__ __forceinline__ void load_step(const unsigned *bits, int64_t n, int64_t b0, int tid,
-                                          unsigned (&v)[kTopkPer]) {
-#pragma unroll
-    for (int e = 0; e < kTopkPer; ++e) {
-        const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
-        v[e] = i < n ? bits[i] : 0u;
+// the list of (head, list) workgroup index `lid`, and this workgroup's range
+struct TopkList {
+    const unsigned *bits;           // scores >= 0: bit order = value order
+    int32_t *out;
+    int64_t n, f, k;                // candidates [f, n), k of them to pick
+    int64_t lo, hi;                 // this workgroup's range of candidates
+    unsigned *st;
+};
+__device__ __forceinline__ TopkList topk_list(const TopkArgs &a, int lid, int part) {
+    TopkList L;
+    const int h = lid / 2, list = lid % 2;
+    L.n = a.S;
+    const int budget = a.budget[list];
+    L.bits = (const unsigned *)(a.score[list] + (int64_t)h * L.n);
+    L.out = a.out[list] + (int64_t)h * budget;
+    L.f = min((int64_t)min(a.forced, budget), L.n);
+    L.k = budget - L.f;
+    const int64_t len = (L.n - L.f + kTopkParts - 1) / kTopkParts;
+    L.lo = min(L.n, L.f + part * len);
+    L.hi = min(L.n, L.lo + len);
+    L.st = a.state + lid * 4;
+    return L;
+}
+
+// grid (Hq * 2) blocks of kTopkBlock threads
+__global__ __launch_bounds__(kTopkBlock) void est_topk_init(TopkArgs a) {
+    const int lid = blockIdx.x, tid = threadIdx.x;
+    const TopkList L = topk_list(a, lid, 0);
+    for (int64_t i = tid; i < L.f; i += kTopkBlock) L.out[i] = (int32_t)i;
+    a.hist[lid * 256 + tid] = 0u;                       // kTopkBlock == 256 bins
+    bool active = L.k > 0;
+    if (active && L.n - L.f <= L.k) {                   // every candidate
+        for (int64_t i = L.f + tid; i < L.n; i += kTopkBlock) L.out[i] = (int32_t)i;
+        active = false;
+    }
+    if (tid == 0) {
+        L.st[0] = 0u;
+        L.st[1] = 0u;
+        L.st[2] = L.k > 0 ? (unsigned)L.k : 0u;
+        L.st[3] = active ? 1u : 0u;
     }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void est_topk_kernel(TopkArgs a) {
-    __shared__ unsigned hist[256];
-    __shared__ int wsum[kTopkThreads / 64];
-    __shared__ unsigned sel_bin, sel_above;
+// grid (kTopkParts, Hq * 2)
+__global__ __launch_bounds__(kTopkBlock) void est_topk_hist(TopkArgs a, int shift) {
+    __shared__ unsigned lh[256];
+    const int lid = blockIdx.y, tid = threadIdx.x;
+    const TopkList L = topk_list(a, lid, blockIdx.x);
+    if (L.st[3] == 0u) return;
+    const unsigned prefix = L.st[0], pmask = L.st[1];
+    lh[tid] = 0u;
+    __syncthreads();
+    for (int64_t b0 = L.lo; b0 < L.hi; b0 += kTopkStep) {
+        unsigned v[kTopkPer];
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+            const int64_t i = b0 + (int64_t)e * kTopkBlock + tid;
+            v[e] = i < L.hi ? L.bits[i] : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < kTopkPer; ++e) {
+            const int64_t i = b0 + (int64_t)e * kTopkBlock + tid;
+            hist_add(lh, (v[e] >> shift) & 255u, i < L.hi && (v[e] & pmask) == prefix);
+        }
+    }
+    __syncthreads();
+    if (lh[tid] != 0u) atomicAdd(&a.hist[lid * 256 + tid], lh[tid]);
+}
+
+// grid (Hq * 2)
+__global__ __launch_bounds__(kTopkBlock) void est_topk_select(TopkArgs a, int shift) {
+    __shared__ unsigned gh[256];
+    const int lid = blockIdx.x, tid = threadIdx.x;
+    unsigned *st = a.state + lid * 4;
+    if (st[3] == 0u) return;
+    gh[tid] = a.hist[lid * 256 + tid];
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned remaining = st[2];
+        unsigned above = 0;
+        int bin = 255;
+        for (; bin > 0; --bin) {
+            if (above + gh[bin] >= remaining) break;
+            above += gh[bin];
+        }
+        st[0] |= (unsigned)bin << shift;
+        st[1] |= 255u << shift;
+        st[2] = remaining - above;
+    }
+    a.hist[lid * 256 + tid] = 0u;                       // for the next pass
+}
+
+// grid (kTopkParts, Hq * 2)
+__global__ __launch_bounds__(kTopkBlock) void est_topk_count(TopkArgs a) {
+    __shared__ int wsum[kTopkBlock / 64];
+    const int lid = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
+    const TopkList L = topk_list(a, lid, part);
+    if (L.st[3] == 0u) return;
+    const unsigned prefix = L.st[0];
+    int gt = 0, eq = 0;
+    for (int64_t i = L.lo + tid; i < L.hi; i += kTopkBlock) {
+        const unsigned b = L.bits[i];
+        gt += b > prefix;
+        eq += b == prefix;
+    }
+    int tg, te;
+    block_scan<kTopkBlock>(gt, &tg, wsum);
+    block_scan<kTopkBlock>(eq, &te, wsum);
+    if (tid == 0) {
+        a.counts[(lid * kTopkParts + part) * 2] = tg;
+        a.counts[(lid * kTopkParts + part) * 2 + 1] = te;
+    }
+}
+
+// grid (kTopkParts, Hq * 2)
+__global__ __launch_bounds__(kTopkBlock) void est_topk_write(TopkArgs a) {
+    __shared__ int wsum[kTopkBlock / 64];
     __shared__ unsigned stage[kTopkStep];
-    const int h = blockIdx.x, list = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int64_t n = a.S;
-    const int budget = a.budget[list];
-    const unsigned *bits = (const unsigned *)(a.score[list] + (int64_t)h * n);   // scores >= 0: bit order = value order
-    int32_t *out = a.out[list] + (int64_t)h * budget;
-    const int f = min((int64_t)min(a.forced, budget), n);
-    for (int i = tid; i < f; i += kTopkThreads) out[i] = i;
-    const int64_t k = budget - f;                        // to pick from [f, n)
-    if (k <= 0) return;
-    if (n - f <= k) {                                  // every candidate
-        for (int64_t i = f + tid; i < n; i += kTopkThreads) out[i] = (int32_t)i;
-        return;
+    const int lid = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
+    const TopkList L = topk_list(a, lid, part);
+    if (L.st[3] == 0u) return;
+    const unsigned prefix = L.st[0];
+    const int R = (int)L.st[2];                        // equal bits to take, smallest indices first
+    int gt_before = 0, eq_before = 0;                  // in the earlier ranges
+    for (int b = 0; b < part; ++b) {
+        gt_before += a.counts[(lid * kTopkParts + b) * 2];
+        eq_before += a.counts[(lid * kTopkParts + b) * 2 + 1];
     }
-    // radix select, 8 bits per pass from the top: the k-th largest bit pattern
-    unsigned prefix = 0, pmask = 0;
-    unsigned remaining = (unsigned)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
-        __syncthreads();
-        // the next step's scores load while this step's are counted
-        unsigned v[kTopkPer], vn[kTopkPer];
-        load_step(bits, n, f, tid, v);
-        for (int64_t b0 = f; b0 < n; b0 += kTopkStep) {
-            if (b0 + kTopkStep < n) load_step(bits, n, b0 + kTopkStep, tid, vn);
+    int64_t pos = L.f + gt_before + min(eq_before, R);
+    int ties = eq_before;                              // equal bits seen before this step
+    // per step, thread t owns the kTopkPer consecutive indices b0 + 8t ..; one
+    // scan of its packed (above, equal) counts places all of its picks
+    for (int64_t b0 = L.lo; b0 < L.hi; b0 += kTopkStep) {
 #pragma unroll
-            for (int e = 0; e < kTopkPer; ++e) {
-                const int64_t i = b0 + (int64_t)e * kTopkThreads + tid;
-                hist_add(hist, (v[e] >> shift) & 255u, i < n && (v[e] & pmask) == prefix);
-            }
-#pragma unroll
-            for (int e = 0; e < kTopkPer; ++e) v[e] = vn[e];
+        for (int e = 0; e < kTopkPer; ++e) {
+            const int64_t i = b0 + (int64_t)e * kTopkBlock + tid;
+            stage[e * kTopkBlock + tid] = i < L.hi ? L.bits[i] : 0u;
         }
-        __syncthreads();
-        if (tid == 0) {
-            unsigned above = 0;
-            int bin = 255;
-            for (; bin > 0; --bin) {
-                if (above + hist[bin] >= remaining) break;
-                above += hist[bin];
-            }
-            sel_bin = (unsigned)bin;
-            sel_above = above;
-        }
-        __syncthreads();
-        prefix |= sel_bin << shift;
-        pmask |= 255u << shift;
-        remaining -= sel_above;
-        __syncthreads();
-    }
-    // bits > prefix are all taken; `remaining` of the bits == prefix, the
-    // smallest indices first; written in index order after the forced head.
-    // Per step, thread t owns the kTopkPer consecutive indices b0 + 8t ..; one
-    // scan of its packed (greater, equal) counts places all of its picks.
-    const int R = (int)remaining;
-    int pos = f;
-    int ties = 0;                                      // equal bits seen before this step
-    unsigned cv[kTopkPer], cn[kTopkPer];
-    load_step(bits, n, f, tid, cv);
-    for (int64_t b0 = f; b0 < n && pos < budget; b0 += kTopkStep) {
-#pragma unroll
-        for (int e = 0; e < kTopkPer; ++e) stage[e * kTopkThreads + tid] = cv[e];
-        if (b0 + kTopkStep < n) load_step(bits, n, b0 + kTopkStep, tid, cn);
         __syncthreads();
         unsigned w[kTopkPer];
         int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < kTopkPer; ++e) {
             w[e] = stage[kTopkPer * tid + e];
-            const bool valid = b0 + kTopkPer * tid + e < n;
+            const bool valid = b0 + kTopkPer * tid + e < L.hi;
             gt += valid && w[e] > prefix;
             eq += valid && w[e] == prefix;
         }
         const int packed = gt | (eq << 16);            // both < 2^16: no carry between the halves
         int total;
-        const int excl = block_scan(packed, &total, wsum) - packed;
+        const int excl = block_scan<kTopkBlock>(packed, &total, wsum) - packed;
         const int r_left = max(R - ties, 0);           // equal bits still to take
         int eq_seen = excl >> 16;
-        int o = pos + (excl & 0xffff) + min(eq_seen, r_left);
+        int64_t o = pos + (excl & 0xffff) + min(eq_seen, r_left);
 #pragma unroll
         for (int e = 0; e < kTopkPer; ++e) {
             const int64_t i = b0 + kTopkPer * tid + e;
-            if (i >= n) break;
+            if (i >= L.hi) break;
             bool take = w[e] > prefix;
             if (w[e] == prefix) {
                 take = eq_seen < r_left;
                 ++eq_seen;
             }
-            if (take) out[o++] = (int32_t)i;
+            if (take) L.out[o++] = (int32_t)i;
         }
         const int tot_gt = total & 0xffff, tot_eq = total >> 16;
         pos += tot_gt + min(tot_eq, r_left);
         ties += tot_eq;
-#pragma unroll
-        for (int e = 0; e < kTopkPer; ++e) cv[e] = cn[e];
         __syncthreads();                               // stage is rewritten next step
     }
 }
@@ -526,8 +598,12 @@ static int launch_est_t(const Problem &p, int n_last, const void *q, const void 
     return (int)hipGetLastError();
 }
 
-size_t est_scratch_bytes(const Problem &p) {
+// row statistics and combined rows, then the selection's histograms, state and counts
+static size_t est_rows_bytes(const Problem &p) {
     return ((size_t)p.Hq * kEstRows * kEstMaxSplits * 2 + (size_t)p.Hq * kEstRows * 2) * sizeof(float);
+}
+size_t est_scratch_bytes(const Problem &p) {
+    return est_rows_bytes(p) + (size_t)p.Hq * 2 * (256 + 4 + kTopkParts * 2) * 4;
 }
 
 int launch_vs_estimate(const Problem &p, int n_last, int n_vertical, int n_slash, int n_forced, const void *q,
@@ -550,7 +626,23 @@ int launch_vs_estimate(const Problem &p, int n_last, int n_vertical, int n_slash
     t.budget[1] = n_slash;
     t.forced = n_forced;
     t.S = p.S;
-    hipLaunchKernelGGL(est_topk_kernel, dim3((unsigned)p.Hq, 2), dim3(kTopkThreads), 0, (hipStream_t)stream, t);
+    char *sel = (char *)ws + scratch + est_rows_bytes(p);
+    t.hist = (unsigned *)sel;
+    t.state = t.hist + (size_t)p.Hq * 2 * 256;
+    t.counts = (int32_t *)(t.state + (size_t)p.Hq * 2 * 4);
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned lists = (unsigned)(p.Hq * 2);
+    hipLaunchKernelGGL(est_topk_init, dim3(lists), dim3(kTopkBlock), 0, s, t);
+    if ((err = (int)hipGetLastError())) return err;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hipLaunchKernelGGL(est_topk_hist, dim3(kTopkParts, lists), dim3(kTopkBlock), 0, s, t, shift);
+        if ((err = (int)hipGetLastError())) return err;
+        hipLaunchKernelGGL(est_topk_select, dim3(lists), dim3(kTopkBlock), 0, s, t, shift);
+        if ((err = (int)hipGetLastError())) return err;
+    }
+    hipLaunchKernelGGL(est_topk_count, dim3(kTopkParts, lists), dim3(kTopkBlock), 0, s, t);
+    if ((err = (int)hipGetLastError())) return err;
+    hipLaunchKernelGGL(est_topk_write, dim3(kTopkParts, lists), dim3(kTopkBlock), 0, s, t);
     return (int)hipGetLastError();
 }
 
