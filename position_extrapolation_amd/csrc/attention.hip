@@ -164,7 +164,14 @@ struct WaveCtx {
 // reads the buffer. The asm has no register outputs; M0 is set inside the
 // block with the one wait state an SALU write of M0 needs before an LDS DMA
 // reads it.
-template <typename T, int D, int NW>
+// Two address forms, the same addresses: SADDR takes the piece's wave-uniform
+// base in an SGPR pair plus the lane's 16-byte offset in one VGPR, shared by
+// every piece and both tensors; otherwise each piece's 64-bit per-lane
+// address is formed in VGPRs. SADDR frees VGPRs (the fused-rotation and
+// vertical-slash kernels need them to keep their score start tuple without
+// spilling) at the cost of SGPRs; the dense kernel with rotated variants
+// runs faster with the VGPR form.
+template <typename T, int D, int NW, bool SADDR>
 __device__ __forceinline__ void dma_tile(const WaveCtx &c, const char *base, int kt, uint32_t dst) {
     constexpr int TILE_BYTES = 2 * kBlk * D * (int)sizeof(T);
     constexpr int WAVE_CHUNKS = TILE_BYTES / 1024 / NW;
@@ -172,15 +179,24 @@ __device__ __forceinline__ void dma_tile(const WaveCtx &c, const char *base, int
 #pragma unroll
     for (int i = 0; i < WAVE_CHUNKS; ++i) {
         const int chunk = c.wave * WAVE_CHUNKS + i;
-        const char *src = base + (int64_t)kt * TILE_BYTES + chunk * 1024 + c.lane * 16;
+        const char *src = base + (int64_t)kt * TILE_BYTES + chunk * 1024;
         const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(dst + chunk * 1024);
-        asm volatile(
-            "s_mov_b32 m0, %1\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %0, off"
-            :
-            : "v"(src), "s"(lds_addr)
-            : "memory", "m0");
+        if constexpr (SADDR)
+            asm volatile(
+                "s_mov_b32 m0, %2\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %0, %1"
+                :
+                : "v"(c.lane * 16), "s"(src), "s"(lds_addr)
+                : "memory", "m0");
+        else
+            asm volatile(
+                "s_mov_b32 m0, %1\n\t"
+                "s_nop 0\n\t"
+                "global_load_lds_dwordx4 %0, off"
+                :
+                : "v"(src + c.lane * 16), "s"(lds_addr)
+                : "memory", "m0");
     }
 }
 
@@ -209,9 +225,26 @@ __device__ __forceinline__ int region_of_tile(const WaveCtx &c, int kt) {
 // the one tile of a wave that can hold keys past its rows
 __device__ __forceinline__ bool is_diag(const WaveCtx &c, int kt) { return kt * kTile + kTile - 1 > c.r0; }
 
+// The lane's index within its wave, formed afresh where it is used: asm, so
+// that the compiler neither hoists it nor keeps values derived from it live
+// across the tile loop (the rare paths that use it recompute theirs).
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Causal mask of the tile that holds this wave's diagonal (keys past the row).
+// FRESH: the lane terms come from fresh_lane(), not from registers kept live.
+template <bool FRESH>
 __device__ __forceinline__ void mask_diag(const WaveCtx &c, int j0, f32x16 (&s)[2]) {
-    const int lim = c.r0 + c.x - j0 - 4 * c.gsel;     // key offset k is kept iff k <= lim
+    int lim;                                          // key offset k is kept iff k <= lim
+    if constexpr (FRESH) {
+        const int ln = fresh_lane();
+        lim = c.r0 + ln % 32 - j0 - 4 * (ln / 32);
+    } else {
+        lim = c.r0 + c.x - j0 - 4 * c.gsel;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -232,13 +265,14 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, const WaveCtx &c, Wave
     constexpr int NU = WaveState<T, D>::NU;
     if (region == st.region) return;
     if constexpr (FUSED) {
-        const int row = c.r0 + c.x;
+        const int ln = fresh_lane();
+        const int row = c.r0 + ln % 32, gsel = ln / 32;
         const bool valid = row < (int)a.S;
-        const T *src = (const T *)a.q_nat + ((c.bh * a.NQ) + (row - a.q0)) * D + E * c.gsel;
+        const T *src = (const T *)a.q_nat + ((c.bh * a.NQ) + (row - a.q0)) * D + E * gsel;
 #pragma unroll
         for (int u = 0; u < NU; ++u) st.qfrag[u] = valid ? *(const vec *)(src + 2 * E * u) : F::zero();
         const int64_t p = region == 0 ? pos_intra(row, a.C) : (region == 1 ? pos_succ(row, a.C, a.W) : pos_inter(a.C, a.W));
-        const float2 *tab = a.table + p * (D / 2) + E * c.gsel;
+        const float2 *tab = a.table + p * (D / 2) + E * gsel;
 #pragma unroll
         for (int u = 0; u < NU / 2; ++u)
 #pragma unroll
@@ -350,8 +384,11 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     st.mref = 0.f;
     st.l_run = 0.f;
     // start of the score accumulators, -mref (0 before the first tile), kept
-    // in registers where they fit: bf16 with materialized query variants
-    constexpr bool C0 = sizeof(T) == 2 && !FUSED;
+    // in registers where they fit: bf16
+    constexpr bool C0 = sizeof(T) == 2;
+    // the fused-rotation kernels take the SGPR-based tile loads and the
+    // recomputed mask terms, which free the registers that tuple needs
+    constexpr bool LEAN = FUSED && sizeof(T) == 2;
     f32x16 c0 = {};
 
     // The per-tile work (QK, mask, softmax step, PV) is written out in both
@@ -371,15 +408,15 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
         t[1] = t[0] >= 0 ? it.next(m[1]) : -1;
         t[2] = t[1] >= 0 ? it.next(m[2]) : -1;
         if (t[0] >= 0) {
-            dma_tile<T, D, NW>(c, c.kbytes, t[0], lds_base);
-            dma_tile<T, D, NW>(c, c.vbytes, t[0], vbase_lds);
+            dma_tile<T, D, NW, true>(c, c.kbytes, t[0], lds_base);
+            dma_tile<T, D, NW, true>(c, c.vbytes, t[0], vbase_lds);
         }
-        if (t[1] >= 0) dma_tile<T, D, NW>(c, c.kbytes, t[1], lds_base + 1u * TILE_BYTES);
+        if (t[1] >= 0) dma_tile<T, D, NW, true>(c, c.kbytes, t[1], lds_base + 1u * TILE_BYTES);
         for (int n = 0; t[0] >= 0; ++n) {
             if (t[1] >= 0) wait_vmcnt<KL>(); else __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();                 // K(n), V(n) landed; V slot (n+1)%2 and K slot (n+2)%3 are free
-            if (t[1] >= 0) dma_tile<T, D, NW>(c, c.vbytes, t[1], vbase_lds + (uint32_t)((n + 1) & 1) * TILE_BYTES);
-            if (t[2] >= 0) dma_tile<T, D, NW>(c, c.kbytes, t[2], lds_base + (uint32_t)((n + 2) % 3) * TILE_BYTES);
+            if (t[1] >= 0) dma_tile<T, D, NW, true>(c, c.vbytes, t[1], vbase_lds + (uint32_t)((n + 1) & 1) * TILE_BYTES);
+            if (t[2] >= 0) dma_tile<T, D, NW, true>(c, c.kbytes, t[2], lds_base + (uint32_t)((n + 2) % 3) * TILE_BYTES);
             const int kt = t[0];
             if (active(c, kt, m[0])) {
                 load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
@@ -390,7 +427,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
                     tile_scores_from<T, D, true>(c.lane, st, c0, kcur, s);
                 else
                     tile_scores<T, D, true>(c.lane, st, kcur, s);
-                if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
+                if (is_diag(c, kt)) mask_diag<true>(c, kt * kTile, s);
                 VFrags<T, D> vf;
                 load_v<T, D>(c.lane, vcur, vf);
                 __builtin_amdgcn_sched_barrier(0);
@@ -432,8 +469,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     }
     auto issue = [&](int kt, int j) __attribute__((always_inline)) {
         const uint32_t slot_addr = lds_base + (uint32_t)(j % NS) * 2 * TILE_BYTES;
-        dma_tile<T, D, NW>(c, c.kbytes, kt, slot_addr);
-        dma_tile<T, D, NW>(c, c.vbytes, kt, slot_addr + TILE_BYTES);
+        dma_tile<T, D, NW, LEAN>(c, c.kbytes, kt, slot_addr);
+        dma_tile<T, D, NW, LEAN>(c, c.vbytes, kt, slot_addr + TILE_BYTES);
     };
 #pragma unroll
     for (int i = 0; i < NS - TPS; ++i)
@@ -462,7 +499,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
                     tile_scores_from<T, D, true>(c.lane, st, c0, cur, s);
                 else
                     tile_scores<T, D, true>(c.lane, st, cur, s);
-                if (is_diag(c, kt)) mask_diag(c, kt * kTile, s);
+                if (is_diag(c, kt)) mask_diag<LEAN>(c, kt * kTile, s);
                 VFrags<T, D> vf;
                 load_v<T, D>(c.lane, cur + TILE_BYTES, vf);
                 __builtin_amdgcn_sched_barrier(0);
