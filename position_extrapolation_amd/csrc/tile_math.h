@@ -83,6 +83,10 @@ __device__ __forceinline__ void tile_scores(int lane, const WaveState<T, D> &st,
 // equal to the start value (-mref, or 0 before the first tile): the first
 // matrix-core op of each accumulator reads c0 and writes a fresh result, so
 // no per-tile initialisation runs on the vector ALU.
+// The wave raises its issue priority for these reads and products: of the
+// two waves sharing a SIMD, the one starting its scores goes first, so the
+// other's softmax and PV fill in behind it rather than the two running the
+// same phase side by side (3% faster dense, 6% vertical-slash, measured).
 template <typename T, int D, bool LDS_SCHED>
 __device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D> &st, const f32x16 &c0,
                                                  const char *__restrict__ kl, f32x16 (&s)[2]) {
@@ -90,6 +94,7 @@ __device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D>
     using vec = typename F::vec;
     constexpr int NU = WaveState<T, D>::NU;
     const vec *k = (const vec *)kl;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = F::mma_from(k[(kb * NU) * 64 + lane], st.qfrag[0], c0);
 #pragma unroll
@@ -106,6 +111,7 @@ __device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D>
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // P = 2^s rounded to the operand type, in PV fragment order; returns this
