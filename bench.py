@@ -397,22 +397,39 @@ def cpu_baseline(name, n_rows=8, seed=0):
                       f"heads, float64 torch-CPU oracle, {dt:.1f} s"}
 
 
+# the files each kernel is compiled from: its source and every header it includes
+KERNEL_SOURCES = {
+    "attention": ["position_extrapolation_amd/csrc/attention.hip", "position_extrapolation_amd/csrc/tile_math.h",
+                  "position_extrapolation_amd/csrc/frag.h", "position_extrapolation_amd/csrc/dca_internal.h",
+                  "include/dca.h"],
+    "remap": ["position_extrapolation_amd/csrc/remap.hip", "position_extrapolation_amd/csrc/frag.h",
+              "position_extrapolation_amd/csrc/dca_internal.h", "include/dca.h"],
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """First 16 hex digits of the SHA-256 over a kernel's source files, in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str, kernel_key: str = ""):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (profiles/traffic.json, already scaled by the copy calibration), or
-    None when the kernel source has changed since they were taken."""
-    import hashlib
-
+    None when the kernel's sources (its file or any header it includes) have
+    changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get("traffic", {}).get(workload + kernel_key)
     if rec is None:
         return None
-    src = "remap.hip" if kernel_key == ":remap" else "attention.hip"
-    field = "remap_source_sha256_16" if kernel_key == ":remap" else "attention_source_sha256_16"
-    digest = hashlib.sha256(open(os.path.join(ROOT, "position_extrapolation_amd", "csrc", src), "rb").read())
-    if digest.hexdigest()[:16] != rec.get(field):
+    kernel = "remap" if kernel_key == ":remap" else "attention"
+    if kernel_source_digest(kernel) != rec.get("sources_sha256_16"):
         return None
     return {"total": rec["read_bytes"] + rec["written_bytes"], "read": rec["read_bytes"],
             "written": rec["written_bytes"]}

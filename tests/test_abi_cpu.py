@@ -234,3 +234,31 @@ def test_status_strings():
     for s in range(5):
         assert api.dca_status_str(s).startswith("DCA_")
     assert api.dca_status_str(99) == "unknown dca_status"
+
+
+def _included_files(path, seen):
+    """Every repository file a source pulls in through #include "..." (recursively)."""
+    seen.add(path)
+    for name in re.findall(r'^#include "([^"]+)"', open(path).read(), flags=re.M):
+        for d in (os.path.dirname(path), os.path.join(ROOT, "include")):
+            cand = os.path.normpath(os.path.join(d, name))
+            if os.path.exists(cand):
+                if cand not in seen:
+                    _included_files(cand, seen)
+                break
+    return seen
+
+
+def test_stored_traffic_is_keyed_on_every_kernel_source():
+    """The bench reports stored HBM traffic only while the kernel's sources are
+    unchanged: the digest must cover the .hip file and every header it includes."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        listed = {os.path.normpath(os.path.join(ROOT, f)) for f in files}
+        reached = _included_files(os.path.normpath(os.path.join(ROOT, files[0])), set())
+        assert reached == listed, (kernel, sorted(reached ^ listed))
+        assert re.fullmatch(r"[0-9a-f]{16}", bench.kernel_source_digest(kernel))
