@@ -87,7 +87,8 @@ __device__ __forceinline__ void tile_scores(int lane, const WaveState<T, D> &st,
 // two waves sharing a SIMD, the one starting its scores goes first, so the
 // other's softmax and PV fill in behind it rather than the two running the
 // same phase side by side (3% faster dense, 6% vertical-slash, measured).
-template <typename T, int D, bool LDS_SCHED>
+// HOLD leaves the priority raised on return; the caller lowers it before PV.
+template <typename T, int D, bool LDS_SCHED, bool HOLD = false>
 __device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D> &st, const f32x16 &c0,
                                                  const char *__restrict__ kl, f32x16 (&s)[2]) {
     using F = Frag<T>;
@@ -111,7 +112,7 @@ __device__ __forceinline__ void tile_scores_from(int lane, const WaveState<T, D>
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!HOLD) __builtin_amdgcn_s_setprio(0);
 }
 
 // P = 2^s rounded to the operand type, in PV fragment order; returns this
