@@ -11,7 +11,8 @@
 //
 // Per workgroup: NW waves x 32 query rows of one query head; 64-key K and V
 // tiles staged through an LDS ring, two tiles per barrier, the next two in
-// flight. Per wave and tile:
+// flight; half the waves run half a tile behind the others, so the two waves
+// of a SIMD are in different phases. Per wave and tile:
 //   S^T (64 keys x 32 rows) = K_rot Q_x^T     2 x (D/16) bf16 MFMA 32x32x16
 //   online softmax (exp2 domain, scale tau * sigma * log2 e); a lane holds 32
 //     scores of one row, the row max is completed with one lane swap
@@ -386,9 +387,10 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     // start of the score accumulators, -mref (0 before the first tile), kept
     // in registers where they fit: bf16
     constexpr bool C0 = sizeof(T) == 2;
-    // the fused-rotation kernels take the SGPR-based tile loads and the
-    // recomputed mask terms, which free the registers that tuple needs
-    constexpr bool LEAN = FUSED && sizeof(T) == 2;
+    // bf16 kernels take the SGPR-based tile loads and the recomputed mask
+    // terms, which free the registers that tuple (and, in the fused kernel,
+    // the rotation) needs
+    constexpr bool LEAN = sizeof(T) == 2;
     f32x16 c0 = {};
 
     // The per-tile work (QK, mask, softmax step, PV) is written out in both
@@ -450,8 +452,92 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
             t[1] = t[2]; m[1] = m[2];
             t[2] = t[1] >= 0 ? it.next(m[2]) : -1;
         }
+    } else if constexpr (TPS == 2) {
+        // Two key tiles per step, lagged pairs. LDS holds a ring of NS = 4
+        // slots of [K tile | V tile]; tile j (in visiting order) lives in slot
+        // j mod 4. Step n computes tiles 2n and 2n+1 and, right after its
+        // barrier, starts the loads of tiles 2n+2 and 2n+3 into the slots of
+        // tiles 2n-2 and 2n-1, which every wave has finished reading: a tile's
+        // K and V are read from LDS only within its own step.
+        // The second half of the waves (one of the two waves on each SIMD) runs
+        // half a tile behind: it leaves the PV product of its step's second
+        // tile, with that tile's V fragments and P in registers, for after the
+        // next barrier. The barrier then no longer lines the two waves of a
+        // SIMD up in the same phase: one's softmax runs under the other's
+        // matrix work. Every row still sees its tiles' QK, softmax and PV in
+        // the same order, so the results are unchanged.
+        static_assert(NS == 4, "lagged ring size");
+        const bool lag = wave >= NW / 2;
+        TileIter<NT> it;
+        it.init(a, h, i0, S, last_row / kTile);
+        int t[4];                        // tiles 2n .. 2n+3 (-1 past the end)
+        unsigned m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[i] = 0;
+            t[i] = (i == 0 || t[i - 1] >= 0) ? it.next(m[i]) : -1;
+        }
+        auto issue = [&](int kt, int j) __attribute__((always_inline)) {
+            const uint32_t slot_addr = lds_base + (uint32_t)(j % NS) * 2 * TILE_BYTES;
+            dma_tile<T, D, NW, LEAN>(c, c.kbytes, kt, slot_addr);
+            dma_tile<T, D, NW, LEAN>(c, c.vbytes, kt, slot_addr + TILE_BYTES);
+        };
+        if (t[0] >= 0) issue(t[0], 0);
+        if (t[1] >= 0) issue(t[1], 1);
+        VFrags<T, D> vf;                 // a lagging wave's pending tile: its V and P
+        vec p[2][NUV];
+        bool pend = false;
+        for (int n = 0; t[0] >= 0; ++n) {
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tiles 2n, 2n+1
+            __syncthreads();                 // ... and everyone's; slots of 2n-2, 2n-1 free
+            if (t[2] >= 0) issue(t[2], 2 * n + 2);
+            if (t[3] >= 0) issue(t[3], 2 * n + 3);
+            if (pend) {
+                tile_pv<T, D>(st, vf, p);
+                pend = false;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int kt = t[i];
+                if (kt >= 0 && active(c, kt, m[i])) {
+                    load_q<T, D, FUSED>(a, c, st, region_of_tile(c, kt));
+                    const char *cur = lds + ((2 * n + i) % NS) * 2 * TILE_BYTES;
+                    f32x16 s[2];
+                    // the raised issue priority is held through the softmax here
+                    if constexpr (C0)
+                        tile_scores_from<T, D, true, true>(c.lane, st, c0, cur, s);
+                    else
+                        tile_scores<T, D, true>(c.lane, st, cur, s);
+                    if (is_diag(c, kt)) mask_diag<LEAN>(c, kt * kTile, s);
+                    load_v<T, D>(c.lane, cur + TILE_BYTES, vf);
+                    __builtin_amdgcn_sched_barrier(0);
+                    float psum = tile_p<T>(s, p);
+                    const bool ok = psum <= kPsumLimit;          // false for inf and NaN too
+                    if (__builtin_amdgcn_ballot_w64(!ok || st.first) != 0) {
+                        raise_ref<T, D>(st, s);
+                        psum = tile_p<T>(s, p);
+                        if constexpr (C0) {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) c0[v] = -st.mref;
+                        }
+                    }
+                    st.l_run += psum;
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(0);
+                    if (lag && i == 1)
+                        pend = true;
+                    else
+                        tile_pv<T, D>(st, vf, p);
+                }
+            }
+            t[0] = t[2]; m[0] = m[2];
+            t[1] = t[3]; m[1] = m[3];
+            t[2] = t[1] >= 0 ? it.next(m[2]) : -1;
+            t[3] = t[2] >= 0 ? it.next(m[3]) : -1;
+        }
+        if (pend) tile_pv<T, D>(st, vf, p);
     } else {
-    // ---- tile window and prologue ---------------------------------------------
+    // ---- other step sizes (fp32 with d = 128: one tile per step) --------------
     // A step handles TPS key tiles between two barriers. LDS holds a ring of NS
     // slots of [K tile | V tile]; tile j (in visiting order) lives in slot
     // j mod NS. Step n uses tiles nTPS .. nTPS+TPS-1 and, once every wave is
@@ -496,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
                 const char *cur = lds + ((n * TPS + i) % NS) * 2 * TILE_BYTES;
                 f32x16 s[2];
                 if constexpr (C0)
-                    tile_scores_from<T, D, true, FUSED>(c.lane, st, c0, cur, s);
+                    tile_scores_from<T, D, true>(c.lane, st, c0, cur, s);
                 else
                     tile_scores<T, D, true>(c.lane, st, cur, s);
                 if (is_diag(c, kt)) mask_diag<LEAN>(c, kt * kTile, s);
@@ -516,9 +602,6 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
                 }
                 st.l_run += psum;
                 __builtin_amdgcn_sched_barrier(0);
-                // the fused kernel holds the raised priority through its softmax
-                // (1.5% faster at 1M, measured; no gain for the other kernels)
-                if constexpr (FUSED) __builtin_amdgcn_s_setprio(0);
                 tile_pv<T, D>(st, vf, p);
             }
         }
