@@ -407,13 +407,25 @@ KERNEL_SOURCES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C/C++ source reduced to its code: comments dropped, whitespace runs
+    collapsed to one space, string literals (inline asm) kept as written."""
+    import re
+
+    tok = re.compile(r'("(?:\\.|[^"\\\n])*")|/\*.*?\*/|//[^\n]*', re.S)
+    code = tok.sub(lambda mt: mt.group(1) if mt.group(1) else " ", src)
+    return " ".join(code.split())
+
+
 def kernel_source_digest(kernel: str) -> str:
-    """First 16 hex digits of the SHA-256 over a kernel's source files, in order."""
+    """First 16 hex digits of the SHA-256 over the code of a kernel's source
+    files, in order (comment-only edits leave it unchanged)."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, f)).read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -168,10 +168,9 @@ struct WaveCtx {
 // Two address forms, the same addresses: SADDR takes the piece's wave-uniform
 // base in an SGPR pair plus the lane's 16-byte offset in one VGPR, shared by
 // every piece and both tensors; otherwise each piece's 64-bit per-lane
-// address is formed in VGPRs. SADDR frees VGPRs (the fused-rotation and
-// vertical-slash kernels need them to keep their score start tuple without
-// spilling) at the cost of SGPRs; the dense kernel with rotated variants
-// runs faster with the VGPR form.
+// address is formed in VGPRs. SADDR frees VGPRs at the cost of SGPRs: the
+// bf16 kernels take it (they need the registers for their score start tuple
+// and, fused, the rotation); the fp32 ones keep the VGPR form.
 template <typename T, int D, int NW, bool SADDR>
 __device__ __forceinline__ void dma_tile(const WaveCtx &c, const char *base, int kt, uint32_t dst) {
     constexpr int TILE_BYTES = 2 * kBlk * D * (int)sizeof(T);
@@ -393,8 +392,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerSimd<T, D>)) void dca_attenti
     constexpr bool LEAN = sizeof(T) == 2;
     f32x16 c0 = {};
 
-    // The per-tile work (QK, mask, softmax step, PV) is written out in both
-    // loops below: moved into a shared function or lambda, it changes the
+    // The per-tile work (QK, mask, softmax step, PV) is written out in each of
+    // the loops below: moved into a shared function or lambda, it changes the
     // register allocation and spills.
     if constexpr (SPLIT) {
         // separate rings: K in 3 slots (two tiles ahead), V in 2 (one ahead).

@@ -262,3 +262,17 @@ def test_stored_traffic_is_keyed_on_every_kernel_source():
         reached = _included_files(os.path.normpath(os.path.join(ROOT, files[0])), set())
         assert reached == listed, (kernel, sorted(reached ^ listed))
         assert re.fullmatch(r"[0-9a-f]{16}", bench.kernel_source_digest(kernel))
+
+
+def test_traffic_digest_ignores_comments_but_not_code():
+    """Comments and whitespace do not invalidate stored counters; code does,
+    including the text of inline asm strings."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    base = 'int a = 1;  // a note\nasm volatile("s_nop 0 // kept");\n'
+    assert bench.code_text(base) == bench.code_text('/* header */ int a = 1;\n\n  asm volatile("s_nop 0 // kept");')
+    assert bench.code_text(base) != bench.code_text(base.replace("a = 1", "a = 2"))
+    assert bench.code_text(base) != bench.code_text(base.replace("s_nop 0 //", "s_nop 1 //"))
