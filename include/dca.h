@@ -270,7 +270,18 @@ int dca_attention(void *out, float *lse, int64_t seq, int64_t C, int64_t W,
  *   3 rotated K (scaled as dca_remap states), 4 V (n_kv_heads). dst: device.
  * dca_debug_vs_lists -- copy the tile lists dca_vs_index wrote: vt and dl
  *   are device int32 [n_q_heads][n_tiles] (n_tiles = ceil(seq/64)), counts
- *   device int32 [n_q_heads] each. */
+ *   device int32 [n_q_heads] each.
+ * dca_debug_vs_tiles -- the key tiles the attention kernel visits for one
+ *   group of `group` (1 or 2) 64-row query tiles starting at query tile
+ *   q_tile (a multiple of group) of head `head`, merged from the lists
+ *   dca_vs_index wrote by the kernel's own iterator [mizuki, MInference
+ *   sections: a 64x64 block is computed when a vertical column or a slash
+ *   diagonal crosses it]: kt_out[i] ascending, mask_out[i] bit q set when
+ *   tile kt_out[i] is active for query tile q_tile + q (device int32 /
+ *   uint32 [cap]); *n_out (device int32) receives the full count, of which
+ *   at most cap entries are written. Group 2 is the vertical-slash
+ *   workgroup. The workspace must hold the lists of a dca_vs_index call with
+ *   the same arguments. */
 int dca_debug_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra,
                         int32_t *pq_succ, int32_t *pq_inter, int32_t *pk, void *stream);
 int dca_debug_tile_regions(int64_t seq, int64_t C, uint8_t *out, void *stream);
@@ -281,6 +292,10 @@ int dca_debug_vs_lists(const void *workspace, size_t workspace_bytes, int64_t se
                        int64_t C, int64_t W, const dca_vs_mask *mask, const dca_shape *shape,
                        int32_t *vt, int32_t *vt_count, int32_t *dl, int32_t *dl_count,
                        void *stream);
+int dca_debug_vs_tiles(const void *workspace, size_t workspace_bytes, int64_t seq,
+                       int64_t C, int64_t W, const dca_vs_mask *mask, const dca_shape *shape,
+                       int32_t head, int64_t q_tile, int32_t group, int32_t *kt_out,
+                       uint32_t *mask_out, int32_t cap, int32_t *n_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ EXPORTS = [
     "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode", "dca_fused_workspace_size",
     "dca_prefill_fused", "dca_vs_estimate_workspace_size", "dca_vs_estimate",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
+    "dca_debug_vs_tiles",
 ]
 
 
@@ -77,6 +78,8 @@ _SIGS = {
     "dca_debug_unpack": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _I64, _I64, _I64, _VP, _VP, _VP]),
     "dca_debug_vs_lists": (ctypes.c_int, [_VP, ctypes.c_size_t, _I64, _I64, _I64, _VP, _VP, _VP, _VP,
                                           _VP, _VP, _VP]),
+    "dca_debug_vs_tiles": (ctypes.c_int, [_VP, ctypes.c_size_t, _I64, _I64, _I64, _VP, _VP, ctypes.c_int32,
+                                          _I64, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _VP, _VP]),
 }
 
 
@@ -257,6 +260,16 @@ def dca_debug_vs_lists(workspace, workspace_bytes, seq, C, W, mask, shape, vt, v
     _check(lib().dca_debug_vs_lists(_ptr(workspace), workspace_bytes, seq, C, W, _ref(mask), ctypes.byref(shape),
                                     _ptr(vt), _ptr(vt_count), _ptr(dl), _ptr(dl_count), _stream(stream)),
            "dca_debug_vs_lists")
+
+
+def dca_debug_vs_tiles(workspace, workspace_bytes, seq, C, W, mask, shape, head, q_tile, group, kt_out,
+                       mask_out, n_out, stream=None):
+    """kt_out / mask_out: int32 tensors of the same length (the cap); n_out: one int32."""
+    assert kt_out.numel() == mask_out.numel()
+    _check(lib().dca_debug_vs_tiles(_ptr(workspace), workspace_bytes, seq, C, W, _ref(mask), ctypes.byref(shape),
+                                    head, q_tile, group, _ptr(kt_out), _ptr(mask_out), kt_out.numel(),
+                                    _ptr(n_out), _stream(stream)),
+           "dca_debug_vs_tiles")
 
 
 # ---- convenience --------------------------------------------------------------

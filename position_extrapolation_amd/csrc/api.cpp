@@ -530,4 +530,25 @@ int dca_debug_vs_lists(const void *workspace, size_t workspace_bytes, int64_t se
     return ok();
 }
 
+int dca_debug_vs_tiles(const void *workspace, size_t workspace_bytes, int64_t seq, int64_t C, int64_t W,
+                       const dca_vs_mask *mask, const dca_shape *shape, int32_t head, int64_t q_tile,
+                       int32_t group, int32_t *kt_out, uint32_t *mask_out, int32_t cap, int32_t *n_out,
+                       void *stream) {
+    Problem p;
+    Layout L;
+    if (mask == nullptr) return fail(DCA_E_INVALID, "mask is NULL");
+    int st = make_problem(seq, C, W, shape, mask, &p);
+    if (st) return st;
+    if (head < 0 || head >= p.Hq) return fail(DCA_E_INVALID, "head out of range");
+    if (group != 1 && group != 2) return fail(DCA_E_INVALID, "group must be 1 or 2");
+    if (q_tile < 0 || q_tile >= p.n_tiles || q_tile % group != 0)
+        return fail(DCA_E_INVALID, "q_tile must be a multiple of group below ceil(seq / 64)");
+    if (cap < 1) return fail(DCA_E_INVALID, "cap must be positive");
+    if (!kt_out || !mask_out || !n_out) return fail(DCA_E_INVALID, "output arrays must be non-NULL");
+    if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const int err = launch_debug_vs_tiles(p, workspace, L, head, q_tile, group, kt_out, mask_out, cap, n_out, stream);
+    if (err) return device_fail(err, "tile-order launch");
+    return ok();
+}
+
 }  // extern "C"

@@ -717,4 +717,47 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
                       : launch_attn_t<float, 64, 4, 4, 2>(p, a, stream);
 }
 
+// Read-back of the visiting order: the key tiles that one group of NT query
+// tiles, starting at query tile t0, visits for head h -- the same iterator the
+// attention kernel runs -- each with the bits of the group's query tiles it is
+// active for. One lane; writes at most cap entries and the full count.
+template <int NT>
+__global__ __launch_bounds__(64) void debug_vs_tiles_kernel(AttnArgs a, int h, int t0, int cap, int32_t *kt_out,
+                                                            uint32_t *m_out, int32_t *n_out) {
+    if (threadIdx.x != 0) return;
+    const int S = (int)a.S;
+    const int i0 = t0 * kTile;
+    const int last_row = (i0 + NT * kTile < S ? i0 + NT * kTile : S) - 1;
+    TileIter<NT> it;
+    it.init(a, h, i0, S, last_row / kTile);
+    int n = 0;
+    unsigned m = 0;
+    for (int kt = it.next(m); kt >= 0; kt = it.next(m), ++n) {
+        if (n < cap) {
+            kt_out[n] = kt;
+            m_out[n] = m;
+        }
+    }
+    *n_out = n;
+}
+
+int launch_debug_vs_tiles(const Problem &p, const void *ws, const Layout &L, int head, int64_t q_tile, int group,
+                          int32_t *kt_out, uint32_t *m_out, int32_t cap, int32_t *n_out, void *stream) {
+    AttnArgs a{};
+    a.S = p.q0 + p.NQ;
+    a.sparse = 1;
+    a.vt = (const int32_t *)((const char *)ws + L.vs_vt);
+    a.vt_n = (const int32_t *)((const char *)ws + L.vs_vt_n);
+    a.dl = (const int32_t *)((const char *)ws + L.vs_dl);
+    a.dl_n = (const int32_t *)((const char *)ws + L.vs_dl_n);
+    a.list_stride = (int32_t)p.n_tiles;
+    if (group == 1)
+        hipLaunchKernelGGL(debug_vs_tiles_kernel<1>, dim3(1), dim3(64), 0, (hipStream_t)stream, a, head,
+                           (int)q_tile, (int)cap, kt_out, m_out, n_out);
+    else
+        hipLaunchKernelGGL(debug_vs_tiles_kernel<2>, dim3(1), dim3(64), 0, (hipStream_t)stream, a, head,
+                           (int)q_tile, (int)cap, kt_out, m_out, n_out);
+    return (int)hipGetLastError();
+}
+
 }  // namespace dca

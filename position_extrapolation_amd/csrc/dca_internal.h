@@ -125,6 +125,8 @@ int launch_debug_unpack(const Problem &p, const void *ws, const Layout &L, int w
                         void *stream);
 int launch_debug_vs_lists(const Problem &p, const void *ws, const Layout &L, int32_t *vt,
                           int32_t *vt_n, int32_t *dl, int32_t *dl_n, void *stream);
+int launch_debug_vs_tiles(const Problem &p, const void *ws, const Layout &L, int head, int64_t q_tile, int group,
+                          int32_t *kt_out, uint32_t *m_out, int32_t cap, int32_t *n_out, void *stream);
 const char *hip_error_text(int err);
 
 }  // namespace dca

@@ -230,6 +230,40 @@ def test_estimate_workspace_size():
     assert keys + table + scores < n < keys + table + scores + (8 << 20)
 
 
+def _call_vs_tiles(**over):
+    sh = over.pop("shape", api.make_shape(1, 4, 2, 128, torch.bfloat16))
+    mask = over.pop("mask", api.dca_vs_mask(0x30000000, 0x31000000, 40, 60))
+    args = dict(ws=0x50000000, ws_bytes=1 << 30, seq=4096, C=1024, W=128, head=1, q_tile=4, group=2,
+                kt=0x60000000, m=0x61000000, cap=64, n=0x62000000)
+    args.update(over)
+    return api.lib().dca_debug_vs_tiles(args["ws"], args["ws_bytes"], args["seq"], args["C"], args["W"],
+                                        None if mask is None else ctypes.byref(mask), ctypes.byref(sh),
+                                        args["head"], args["q_tile"], args["group"], args["kt"], args["m"],
+                                        args["cap"], args["n"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mask=None), api.DCA_E_INVALID),
+    (dict(head=4), api.DCA_E_INVALID),
+    (dict(head=-1), api.DCA_E_INVALID),
+    (dict(group=3), api.DCA_E_INVALID),
+    (dict(q_tile=5), api.DCA_E_INVALID),                 # not a multiple of the group
+    (dict(q_tile=64), api.DCA_E_INVALID),                # past ceil(seq / 64)
+    (dict(cap=0), api.DCA_E_INVALID),
+    (dict(n=None), api.DCA_E_INVALID),
+    (dict(ws_bytes=1 << 16), api.DCA_E_WORKSPACE),
+])
+def test_vs_tiles_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_vs_tiles(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_valid_vs_tiles_call_without_gpu_reports_device_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_vs_tiles() == api.DCA_E_DEVICE
+
+
 def test_status_strings():
     for s in range(5):
         assert api.dca_status_str(s).startswith("DCA_")

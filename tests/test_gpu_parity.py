@@ -420,6 +420,61 @@ def test_vs_index_lists_bit_exact(S, nv, ns):
         assert torch.equal(dl[h, :len(rdl)].cpu().long(), rdl)
 
 
+@pytest.mark.parametrize("S,nv,ns,heads,q_tiles", [
+    (4096, 40, 60, range(8), None),                # every query tile
+    (1000, 70, 70, range(8), None),                # ragged: an odd tile count, a half-empty pair
+    (1048576, 1000, 2000, (0, 17, 39), 48),        # the 1M shape: sampled and boundary query tiles
+])
+def test_vs_tile_order_bit_exact(S, nv, ns, heads, q_tiles):
+    """The key tiles the attention kernel's own iterator visits, merged on the
+    device from the per-head lists, against the tile mask defined directly
+    from the columns and offsets (oracle): for one query tile the active
+    tiles kt <= t ascending; for the kernel's two-tile workgroup their union,
+    each with the bit of every query tile it is active for."""
+    say(f"[vs tiles] S={S} nv={nv} ns={ns}")
+    hq = 40 if S >= (1 << 20) else 8
+    w = _wl("qwen14b_1m_vs", seq=S, chunk=1024 if S >= 1024 else 64, window=64, n_vertical=nv, n_slash=ns,
+            n_q_heads=hq, n_kv_heads=hq // 5 if hq == 40 else 2)
+    vert, slash = _vs_case(w, seed=21)
+    shape = api.make_shape(1, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16)
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    mask = api.make_mask(vd, sd)
+    nbytes = api.dca_workspace_size(S, w.chunk, w.window, shape, mask)
+    ws = api.alloc_workspace(nbytes, DEV)
+    api.dca_vs_index(S, w.chunk, w.window, mask, shape, ws, nbytes)
+    nt = (S + 63) // 64
+    kt_out = torch.empty(nt, dtype=torch.int32, device=DEV)
+    m_out = torch.empty(nt, dtype=torch.int32, device=DEV)
+    n_out = torch.empty(1, dtype=torch.int32, device=DEV)
+    if q_tiles is None:
+        tiles = list(range(nt))
+    else:
+        rng = np.random.default_rng(3)
+        tiles = sorted(set([0, 1, 2, 3, nt - 2, nt - 1, nt // 2, nt // 2 + 1]
+                           + [int(x) for x in rng.integers(0, nt, q_tiles)]))
+    checked = 0
+    for h in heads:
+        def active(t):
+            kt = torch.arange(t + 1)
+            return kt[O.vs_tile_active(vert[h], slash[h], torch.full_like(kt, t), kt)]
+        for group in (1, 2):
+            for t0 in sorted(set(t - t % group for t in tiles)):
+                api.dca_debug_vs_tiles(ws, nbytes, S, w.chunk, w.window, mask, shape, h, t0, group,
+                                       kt_out, m_out, n_out)
+                n = int(n_out.item())
+                assert n <= nt
+                got_kt = kt_out[:n].cpu().long()
+                got_m = m_out[:n].cpu().long()
+                per_q = [active(t0 + q) if t0 + q < nt else torch.empty(0, dtype=torch.long) for q in range(group)]
+                union = torch.unique(torch.cat(per_q))
+                assert torch.equal(got_kt, union), (h, t0, group)
+                for q in range(group):
+                    assert torch.equal(got_kt[(got_m >> q) & 1 == 1], per_q[q]), (h, t0, group, q)
+                assert ((got_m >> group) == 0).all()
+                checked += 1
+    say(f"  {checked} tile lists identical")
+
+
 @pytest.mark.parametrize("S,C,W,nv,ns", [(4096, 1024, 128, 40, 60), (1000, 256, 64, 10, 12),
                                          (32768, 8192, 1024, 300, 600)])
 def test_vs_parity(S, C, W, nv, ns):
