@@ -207,6 +207,23 @@ def test_parity_every_key_tile_count(S):
     assert torch.equal(fout, out) and torch.equal(flse, lse)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 1), (40, 1)])
+def test_parity_one_kv_head_for_many_query_heads(Hq, Hkv):
+    """Group sizes past the decode kernel's 32 columns: the prefill's work
+    decode spreads the query heads of one KV head over XCD streams; every
+    head's rows must match the oracle."""
+    say(f"[parity] Hq={Hq} Hkv={Hkv} (G={Hq // Hkv})")
+    w = workloads.Workload("t", 1, Hq, Hkv, 128, 1300, 512, 64, "bf16", 0.5, True)
+    q, k, v = synth.make_qkv(w, seed=Hq, device=DEV)
+    out, lse = _run(q, k, v, w)
+    rows = synth.sample_rows(w.seq, w.chunk, w.window, 96, seed=2)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    err, lerr = _err(out[:, :, rows_t], ref), _err(lse[:, :, rows_t], ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+
+
 def _discrimination(q, k, v, rows, w, ref, gpu_rows):
     """The GPU error must sit far below how far two wrong position mappings
     move the output: vanilla RoPE, and successive-chunk pairs treated as
