@@ -873,6 +873,43 @@ def test_graph_capture_prefill_and_decode():
     _replays_match(dec, [do, dl], [ref_do, ref_dl])
 
 
+def test_graph_capture_fused_and_chunked():
+    """The fused-rotation prefill, and a chunked prefill of two blocks in one
+    graph (the second block reads the keys the first wrote into the
+    workspace), replayed with eager work in between: every replay equals the
+    eager whole-sequence call bit for bit."""
+    w = workloads.Workload("t", 1, 4, 2, 128, 3000, 1024, 128, "bf16", 0.5, True)
+    say(f"[graph] S={w.seq} C={w.chunk} W={w.window}: fused, chunked in two blocks")
+    q, k, v = synth.make_qkv(w, seed=72, device=DEV)
+    shape = api.shape_of(q, k)
+    S, C, W = w.seq, w.chunk, w.window
+    ref_out, ref_lse = _run(q, k, v, w)
+    fbytes = api.dca_fused_workspace_size(S, C, W, shape)
+    fws = api.alloc_workspace(fbytes, DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    _replays_match(lambda: api.dca_prefill_fused(q, k, v, out, lse, S, C, W, w.rope_base, w.yarn_scale, None, shape,
+                                                 fws, fbytes), [out, lse], [ref_out, ref_lse])
+    blk = 1536
+    cbytes = api.dca_chunk_workspace_size(S, blk, C, W, shape)
+    cws = api.alloc_workspace(cbytes, DEV)
+    blocks = []
+    for q0 in (0, blk):
+        n = min(blk, S - q0)
+        ins = tuple(t[:, :, q0:q0 + n].contiguous() for t in (q, k, v))
+        blocks.append((q0, n, ins, torch.empty_like(ins[0]),
+                       torch.empty(q.shape[:2] + (n,), dtype=torch.float32, device=DEV)))
+
+    def chunks():
+        for q0, n, (qb, kb, vb), ob, lb in blocks:
+            api.dca_prefill_chunk(qb, kb, vb, ob, lb, q0, n, S, C, W, w.rope_base, w.yarn_scale, None, shape, cws,
+                                  cbytes)
+
+    outs = [x for b in blocks for x in (b[3], b[4])]
+    refs = [x for q0, n, *_ in blocks for x in (ref_out[:, :, q0:q0 + n], ref_lse[:, :, q0:q0 + n])]
+    _replays_match(chunks, outs, refs)
+
+
 # ---------------------------------------------------------------------------
 # a plain C consumer of the ABI (tests/c_abi_example.c, built by build())
 # ---------------------------------------------------------------------------
