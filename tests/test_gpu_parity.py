@@ -278,6 +278,26 @@ def test_parity_sampled_rows_1m():
     _discrimination(q, k, v, rows, w, ref, out_rows)
 
 
+def test_fused_and_chunked_equal_whole_at_1m():
+    """At the 1M-token Qwen2.5-14B shape, in the launch configurations the
+    benchmark times: the fused-rotation path and the chunked path (32 blocks
+    of 32,768 rows) give the whole-sequence prefill's output and lse bit for
+    bit (whose rows the oracle checks in the test above)."""
+    w = workloads.get("qwen14b_1m")
+    say(f"[1M] fused and chunked against the whole prefill, S={w.seq}")
+    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    out, lse = _run(q, k, v, w)
+    fout, flse = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, return_lse=True, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fout, out) and torch.equal(flse, lse)
+    del fout, flse
+    torch.cuda.empty_cache()
+    cout, clse = api.prefill_chunked(q, k, v, w.chunk, w.window, 32768, w.rope_base, w.yarn_scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cout, out) and torch.equal(clse, lse)
+    say("  fused and chunked outputs and lse identical to the whole prefill")
+
+
 def test_parity_4m_tokens():
     """A 4M-token sequence (2^22; one KV head, d = 64, C = 1M, W = 128K):
     row, tile and byte offsets four times past the benchmark's largest shape.
