@@ -704,6 +704,33 @@ def test_decode_long_context():
     assert dp <= TOL["bf16"]
 
 
+def test_decode_at_1m_context():
+    """Decode the last four tokens of the 1M-token Qwen2.5-14B shape after a
+    chunk-call prefill of the rest, as the benchmark does: the oracle on every
+    decoded row of all 40 heads, and the error far below the distance of
+    vanilla RoPE from the DCA result. (These rows sit at the end of a chunk,
+    past the window, where the successive and inter positions coincide, so
+    the other wrong mapping of the long-context test is no wrong mapping
+    here.)"""
+    w = workloads.get("qwen14b_1m")
+    steps = 4
+    prompt = w.seq - steps
+    say(f"[decode 1M] prompt={prompt} steps={steps}")
+    q, k, v = synth.make_qkv(w, seed=4, device=DEV)
+    out, lse = _decode_run(q, k, v, w, prompt, steps)
+    rows = np.arange(prompt, prompt + steps)
+    ref, ref_lse = _oracle(q, k, v, rows, w)
+    err, lerr = _err(out, ref), _err(lse, ref_lse)
+    say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL["bf16"] and lerr <= 2e-2
+    rows_t = torch.as_tensor(rows)
+    van, _ = O.vanilla_prefill_rows(q[:, :, rows_t.to(q.device)].cpu(), rows_t, k.cpu(), v.cpu(), w.rope_base,
+                                    w.yarn_scale)
+    dv = (van - ref).abs().max().item()
+    say(f"  vanilla RoPE distance {dv:.3e}")
+    assert err <= 0.1 * dv
+
+
 # ---------------------------------------------------------------------------
 # fused query rotation: identical to the path with materialized variants
 # ---------------------------------------------------------------------------
