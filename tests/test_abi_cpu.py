@@ -310,3 +310,35 @@ def test_traffic_digest_ignores_comments_but_not_code():
     assert bench.code_text(base) == bench.code_text('/* header */ int a = 1;\n\n  asm volatile("s_nop 0 // kept");')
     assert bench.code_text(base) != bench.code_text(base.replace("a = 1", "a = 2"))
     assert bench.code_text(base) != bench.code_text(base.replace("s_nop 0 //", "s_nop 1 //"))
+
+
+@pytest.mark.parametrize("S,nv,ns", [(1000, 20, 30), (4096, 40, 60), (3001, 200, 100)])
+def test_bench_sparse_work_count_equals_enumeration(S, nv, ns):
+    """The vertical-slash workload's work (bench.vs_active_pairs, a
+    convolution over the tile lists) equals the causal pairs of every active
+    64x64 tile, enumerated tile by tile with the oracle's activity rule."""
+    import importlib.util
+
+    import numpy as np
+
+    from oracle import dca_oracle as O
+    from position_extrapolation_amd import synth, workloads
+
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    w0 = workloads.get("qwen14b_1m_vs")
+    w = workloads.Workload(**{**w0.__dict__, "seq": S, "n_q_heads": 3, "n_kv_heads": 1,
+                              "n_vertical": nv, "n_slash": ns})
+    vert, slash = synth.vs_mask(w.n_q_heads, S, nv, ns, seed=5)
+    n = (S + 63) // 64
+    brute = 0
+    for h in range(w.n_q_heads):
+        for t in range(n):
+            kt = torch.arange(t + 1)
+            act = O.vs_tile_active(torch.from_numpy(vert[h]), torch.from_numpy(slash[h]),
+                                   torch.full_like(kt, t), kt)
+            rows = min(64, S - 64 * t)
+            for j in kt[act].tolist():
+                brute += rows * (rows + 1) // 2 if j == t else rows * 64
+    assert bench.vs_active_pairs(w, vert, slash) == brute
