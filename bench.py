@@ -26,7 +26,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import statistics
 import sys
@@ -50,14 +49,126 @@ def log(*a):
 
 
 def remap_bytes(w) -> float:
-    """Algorithmic bytes of the pre-pass: read q, k, v once; write three
-    rotated query variants, the rotated keys and the value re-layout; plus
-    the float32 cos/sin table for positions [0, C + W)."""
+    """Algorithmic bytes of the RoPE/DCA pre-pass: read q and k once, write the
+    three rotated query variants and the rotated keys,
+    S B (Hq + Hkv) d e + S B (3 Hq + Hkv) d e (45,056 B per token at the 1M
+    Qwen2.5-14B shape)."""
     e = 2 if w.dtype == "bf16" else 4
-    per_tok = (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim * e           # read
-    per_tok += (3 * w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim * e      # write
-    table = (w.chunk + w.window) * (w.head_dim // 2) * 8
-    return float(per_tok * w.seq * w.batch + table)
+    per_tok = (w.n_q_heads + w.n_kv_heads) * w.head_dim * e               # read
+    per_tok += (3 * w.n_q_heads + w.n_kv_heads) * w.head_dim * e          # write
+    return float(per_tok * w.seq * w.batch)
+
+
+def remap_extra_bytes(w) -> dict:
+    """Bytes the pre-pass moves beyond the algorithmic ones, by design: the
+    value re-layout into the attention kernel's operand order (read and write
+    v once) and the float32 cos/sin table for positions [0, C + W)."""
+    e = 2 if w.dtype == "bf16" else 4
+    return {"value_relayout": float(2 * w.n_kv_heads * w.head_dim * e * w.seq * w.batch),
+            "cos_sin_table": float((w.chunk + w.window) * (w.head_dim // 2) * 8)}
+
+
+class ClockSampler:
+    """The GPU's graphics clock (MHz), sampled every `period` seconds by a
+    host thread while a timed region runs: from amdsmi, else from the sysfs
+    DPM table (the level marked current). stop() returns the summary, or a
+    record of why no clock could be read."""
+
+    def __init__(self, period: float = 0.05):
+        import threading
+
+        self.period = period
+        self.samples = []
+        self.power = []
+        self.source = None
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._open()
+
+    def _open(self):
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0] if len(handles) == 1 else self._match(amdsmi, handles)
+            if h is None:
+                raise RuntimeError(f"{len(handles)} GPUs listed, none matched cuda:0's PCI address")
+            amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            self.source = "amdsmi gfx clock"
+
+            def read():
+                clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
+                try:
+                    pw = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
+                except Exception:
+                    pw = None
+                return clk, pw
+            return read
+        except Exception as e:              # no amdsmi, no permission, no match
+            self.error = f"amdsmi: {e}"
+        import glob
+
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                open(path).read()
+            except OSError:
+                continue
+            self.source = f"sysfs {path}"
+
+            def read(path=path):
+                for line in open(path):
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")), None
+                return None, None
+            return read
+        return None
+
+    @staticmethod
+    def _match(amdsmi, handles):
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        if bus is None:
+            return None
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)        # "dddd:bb:dd.f"
+            if int(bdf.split(":")[1], 16) == int(bus):
+                return h
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                clk, pw = self._read()
+                if clk:
+                    self.samples.append(float(clk))
+                if pw:
+                    self.power.append(float(pw))
+            except Exception as e:
+                self.error = str(e)
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"mhz_mean": None, "source": self.source, "error": self.error or "no clock source"}
+        xs = sorted(self.samples)
+        res = {"mhz_mean": round(sum(xs) / len(xs), 1), "mhz_median": xs[len(xs) // 2], "mhz_min": xs[0],
+               "mhz_max": xs[-1], "samples": len(xs), "source": self.source}
+        if self.power:
+            res["socket_power_w_mean"] = round(sum(self.power) / len(self.power), 1)
+        return res
 
 
 def vs_active_pairs(w, vert, slash) -> float:
@@ -136,12 +247,14 @@ class Runner:
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
+        clock = ClockSampler().start()
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(evs[i])
             log(f"[bench] {self.w.name}: step {i + 1}/{steps} enqueued")
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        self.clock = clock.stop()
         remap_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         index_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
         attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
@@ -167,6 +280,7 @@ def measure(name, steps, warmup, device):
         "flops": flops,
         # per-step times from the stream events (the mean above is the host clock over all steps)
         "step_ms_median": statistics.median(r.step_event_ms), "step_ms_min": r.step_event_ms[0],
+        "clock": r.clock,
     }
     if w.sparse:
         res["vs_index_ms"] = index_ms
@@ -176,6 +290,19 @@ def measure(name, steps, warmup, device):
     del r
     torch.cuda.empty_cache()
     return w, res
+
+
+def clock_line(clock, achieved_tflops):
+    """The sampled clock beside the roofline: the bf16 dense MFMA rate at that
+    clock (256 CUs x 4096 flop per clock) and the attention kernel's share of
+    it, so that a gap between two runs reads as clock or as code."""
+    res = dict(clock)
+    mhz = clock.get("mhz_mean")
+    if mhz:
+        at_clock = 256 * 4096 * mhz * 1e6 / 1e12
+        res["bf16_peak_at_clock_tflops"] = round(at_clock, 1)
+        res["attention_frac_at_clock"] = round(achieved_tflops / at_clock, 4)
+    return res
 
 
 def measure_chunked(name, chunk, steps, warmup, device):
@@ -380,10 +507,24 @@ def measure_decode(name, steps, device):
     return res
 
 
-def cpu_baseline(name, n_rows=8, seed=0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(name, n_rows=64, seed=0):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
-    n_rows query rows spread over the sequence, every head. Reported in the
-    benchmark's unit (TFLOP/s of the sampled rows' causal work)."""
+    n_rows query rows spread evenly over the sequence, every head. Reported in
+    the benchmark's unit (TFLOP/s of the sampled rows' causal work, 4 d flops
+    per causal pair and head), with the time a full prefill would take at the
+    same rate (time x total pairs / sampled pairs), labelled as such."""
     from oracle import dca_oracle as O
 
     w = workloads.get(name)
@@ -397,10 +538,20 @@ def cpu_baseline(name, n_rows=8, seed=0):
     t0 = time.perf_counter()
     O.dca_prefill_rows(q_rows, rows, kc, vc, w.chunk, w.window, w.rope_base, w.yarn_scale)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * w.n_q_heads * w.batch * float((rows + 1).sum())
+    pairs = float((rows + 1).sum()) * w.n_q_heads * w.batch
+    total_pairs = w.n_q_heads * w.batch * w.seq * (w.seq + 1) / 2.0
+    flops = 4.0 * w.head_dim * pairs
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_rows} query rows evenly spread over {w.name} (S={w.seq}), all {w.n_q_heads} "
-                      f"heads, float64 torch-CPU oracle, {dt:.1f} s"}
+                      f"heads, float64 torch-CPU oracle on {threads} threads, {dt:.1f} s",
+            "seconds": round(dt, 2), "causal_pairs": pairs, "cpu_model": cpu_model(),
+            "host_logical_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "extrapolated_full_prefill_s": round(dt * total_pairs / pairs, 1),
+            "extrapolation": "sample time x total causal pairs / sampled causal pairs (not measured)"}
 
 
 # the files each kernel is compiled from: its source and every header it includes
@@ -477,7 +628,7 @@ def main():
     ap.add_argument("--only", choices=["decode", "chunked", "fused", "estimate", "online"],
                     help="run just this 1M measurement and print its JSON (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -508,7 +659,7 @@ def main():
     if not args.no_extra:
         for name in ("qwen7b_128k", "qwen14b_1m_vs"):
             if name != args.workload:
-                steps = 10 if name == "qwen7b_128k" else max(1, args.steps)
+                steps = 10 if name == "qwen7b_128k" else min(5, max(1, args.steps))
                 extra.append(measure(name, steps, 2 if name == "qwen7b_128k" else 1, dev)[1])
         extra.append(measure_chunked("qwen14b_1m", 32768, 1, 1, dev))
         extra.append(measure_decode("qwen14b_1m", 64, dev))
@@ -547,7 +698,10 @@ def main():
                   "achieved": round(main_res["remap_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                   "frac": round(main_res["remap_gbs"] / PEAK_HBM_GBS, 4),
                   "algorithmic_bytes": remap_bytes(w),
+                  # moved as well, by design, and not counted in `achieved`
+                  "extra_bytes": remap_extra_bytes(w),
                   "traffic": None if remap_traffic is None else remap_traffic["total"]},
+        "clock": clock_line(main_res["clock"], achieved),
         "attention_ms": round(main_res["attention_ms"], 3),
         "step_ms_median": round(main_res["step_ms_median"], 3),
         "step_ms_min": round(main_res["step_ms_min"], 3),

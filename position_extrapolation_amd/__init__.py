@@ -6,4 +6,4 @@ problem shapes, `synth` the seeded input generators.
 """
 
 from . import api, synth, workloads  # noqa: F401
-from .api import prefill, yarn_logit_scale  # noqa: F401
+from .api import prefill  # noqa: F401

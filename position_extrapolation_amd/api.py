@@ -9,7 +9,6 @@ no fallback path -- a missing library raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -136,10 +135,34 @@ def shape_of(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0) -> dc
     return make_shape(q.shape[0], q.shape[1], k.shape[1], q.shape[3], q.dtype, softmax_scale)
 
 
-def make_mask(vertical: torch.Tensor | None, slash: torch.Tensor | None) -> dca_vs_mask | None:
-    """vertical [Hq, nv], slash [Hq, ns]: device int32 tensors (kept alive by the caller)."""
+def _check_list(t: torch.Tensor, name: str, n_q_heads: int | None):
+    """The library reads n_q_heads x n entries of a mask list from device
+    memory at h * n + e: anything but a contiguous 2-D int32 device tensor of
+    that many rows would be read wrongly or past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32 (got {t.dtype})")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [n_q_heads, n] tensor (got shape {tuple(t.shape)})")
+    if n_q_heads is not None and t.shape[0] != n_q_heads:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the queries have {n_q_heads} heads")
+
+
+def make_mask(vertical: torch.Tensor | None, slash: torch.Tensor | None,
+              n_q_heads: int | None = None) -> dca_vs_mask | None:
+    """vertical [Hq, nv], slash [Hq, ns]: contiguous device int32 tensors (kept
+    alive by the caller); n_q_heads, when given, must equal their row count."""
     if vertical is None and slash is None:
         return None
+    if vertical is not None:
+        _check_list(vertical, "vertical", n_q_heads)
+    if slash is not None:
+        _check_list(slash, "slash", n_q_heads)
+    if vertical is not None and slash is not None and vertical.device != slash.device:
+        raise ValueError("vertical and slash must be on one device")
     nv = 0 if vertical is None else vertical.shape[1]
     ns = 0 if slash is None else slash.shape[1]
     return dca_vs_mask(_ptr(vertical), _ptr(slash), nv, ns)
@@ -281,12 +304,6 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return buf[off:off + nbytes]
 
 
-def yarn_logit_scale(seq: int, C: int) -> float:
-    """The YaRN-style logit temperature max(1, 0.1 ln(seq / C) + 1)
-    [mizuki, DCA + YaRN]."""
-    return max(1.0, 0.1 * math.log(seq / C) + 1.0)
-
-
 def prefill(q, k, v, C: int, W: int, rope_base: float = 1e7, yarn_scale: float = 1.0,
             vertical=None, slash=None, return_lse: bool = False, softmax_scale: float = 0.0,
             workspace: torch.Tensor | None = None, fused: bool = False):
@@ -300,7 +317,7 @@ def prefill(q, k, v, C: int, W: int, rope_base: float = 1e7, yarn_scale: float =
             raise ValueError("q, k and v must be contiguous")
     seq = q.shape[2]
     shape = shape_of(q, k, softmax_scale)
-    mask = make_mask(vertical, slash)
+    mask = make_mask(vertical, slash, q.shape[1])
     size = dca_fused_workspace_size if fused else dca_workspace_size
     nbytes = size(seq, C, W, shape, mask)
     if workspace is None or workspace.numel() < nbytes:
@@ -321,7 +338,7 @@ def prefill_chunked(q, k, v, C: int, W: int, chunk: int, rope_base: float = 1e7,
         raise ValueError("chunk must be a positive multiple of 64")
     seq = q.shape[2]
     shape = shape_of(q, k, softmax_scale)
-    mask = make_mask(vertical, slash)
+    mask = make_mask(vertical, slash, q.shape[1])
     nbytes = dca_chunk_workspace_size(seq, min(chunk, seq), C, W, shape, mask)
     workspace = alloc_workspace(nbytes, q.device)
     out = torch.empty_like(q)

@@ -155,6 +155,21 @@ static int check_workspace(const Problem &p, const void *ws, size_t bytes, Layou
     return DCA_OK;
 }
 
+// The pre-pass writes the workspace while it reads the inputs (and the
+// fused-rotation kernel reads q beside the workspace): an input inside the
+// workspace would be overwritten mid-read. q is [B][Hq][NQ][D], k and v
+// [B][Hkv][NQ][D] for the call's rows.
+static int check_inputs_vs_workspace(const Problem &p, const void *const *inputs, int n_inputs, const void *ws,
+                                     size_t ws_bytes) {
+    static const char *const names[3] = {"q", "k", "v"};
+    for (int i = 0; i < n_inputs; ++i) {
+        const size_t ib = (size_t)p.B * (i == 0 ? p.Hq : p.Hkv) * p.NQ * p.D * p.esize;
+        if (overlaps(ws, ws_bytes, inputs[i], ib))
+            return fail(DCA_E_INVALID, "%s overlaps the workspace", names[i]);
+    }
+    return DCA_OK;
+}
+
 }  // namespace dca
 
 using namespace dca;
@@ -229,6 +244,8 @@ int dca_remap(const void *q, const void *k, const void *v, int64_t seq, int64_t 
     if ((st = check_rope(rope_base))) return st;
     if ((st = check_yarn(yarn_scale))) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    const void *inputs[3] = {q, k, v};
+    if ((st = check_inputs_vs_workspace(p, inputs, 3, workspace, workspace_bytes))) return st;
     if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     return ok();
 }
@@ -258,6 +275,7 @@ static int check_outputs(const Problem &p, const void *out, const float *lse, co
         if (overlaps(out, obytes, inputs[i], ib)) return fail(DCA_E_INVALID, "out overlaps an input");
         if (overlaps(lse, lbytes, inputs[i], ib)) return fail(DCA_E_INVALID, "lse overlaps an input");
     }
+    if (int st = check_inputs_vs_workspace(p, inputs, n_inputs, ws, ws_bytes)) return st;
     if (overlaps(out, obytes, ws, ws_bytes)) return fail(DCA_E_INVALID, "out overlaps the workspace");
     if (overlaps(lse, lbytes, ws, ws_bytes)) return fail(DCA_E_INVALID, "lse overlaps the workspace");
     if (overlaps(lse, lbytes, out, obytes)) return fail(DCA_E_INVALID, "lse overlaps out");
@@ -432,6 +450,8 @@ int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, d
     if (((uintptr_t)workspace & 255) != 0) return fail(DCA_E_INVALID, "workspace must be 256-byte aligned");
     if (workspace_bytes < total)
         return fail(DCA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, total);
+    const void *inputs[2] = {q, k};
+    if ((st = check_inputs_vs_workspace(p, inputs, 2, workspace, workspace_bytes))) return st;
     const Layout L = layout_for(p);
     float *ws_scores = (float *)((char *)workspace + scores);   // [2][Hq][seq], used for absent outputs
     float *vs = vertical_score ? vertical_score : ws_scores;

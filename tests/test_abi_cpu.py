@@ -87,6 +87,9 @@ def _call_prefill(**over):
     (dict(out=0x10000000), api.DCA_E_INVALID),            # out aliases q
     (dict(out=0x50000000 + 4096), api.DCA_E_INVALID),     # out inside the workspace
     (dict(lse=0x40000000 + 100), api.DCA_E_INVALID),      # lse inside out
+    (dict(q=0x50000000 + 4096), api.DCA_E_INVALID),       # q inside the workspace
+    (dict(k=0x50000000 + (1 << 29)), api.DCA_E_INVALID),  # k inside the workspace
+    (dict(v=0x50000000 - 4096), api.DCA_E_INVALID),       # v runs into the workspace
     (dict(shape=api.make_shape(1, 3, 2, 64, torch.float32)), api.DCA_E_INVALID),
     (dict(shape=api.make_shape(1, 2, 1, 96, torch.float32)), api.DCA_E_UNSUPPORTED),
     (dict(shape=api.make_shape(0, 2, 1, 64, torch.float32)), api.DCA_E_INVALID),
@@ -152,6 +155,7 @@ def _call_chunk(**over):
     (dict(ws_bytes=1 << 20), api.DCA_E_WORKSPACE),
     (dict(out=0x10000000 + 4096), api.DCA_E_INVALID),     # out overlaps q
     (dict(k=None), api.DCA_E_INVALID),
+    (dict(v=0x50000000 + 256), api.DCA_E_INVALID),        # v inside the workspace
 ])
 def test_chunk_arguments_rejected_before_any_hip_call(over, status):
     assert _call_chunk(**over) == status
@@ -182,6 +186,7 @@ def _call_decode(**over):
     (dict(shape=api.make_shape(1, 66, 2, 64, torch.float32)), api.DCA_E_UNSUPPORTED),   # 33 heads per group
     (dict(out=0x30000000), api.DCA_E_INVALID),            # out aliases v
     (dict(yarn=-1.0), api.DCA_E_INVALID),
+    (dict(q=0x50000000 + 4096), api.DCA_E_INVALID),       # the new query inside the cache workspace
 ])
 def test_decode_arguments_rejected_before_any_hip_call(over, status):
     assert _call_decode(**over) == status
@@ -214,6 +219,7 @@ def _call_estimate(**over):
     (dict(shape=api.make_shape(2, 4, 2, 64, torch.float32)), api.DCA_E_UNSUPPORTED),   # batch 2
     (dict(ws_bytes=1 << 20), api.DCA_E_WORKSPACE),
     (dict(slash=0x30000000 + 64), api.DCA_E_INVALID),     # lists overlap
+    (dict(k=0x50000000 + 4096), api.DCA_E_INVALID),       # k inside the workspace
 ])
 def test_estimate_arguments_rejected_before_any_hip_call(over, status):
     assert _call_estimate(**over) == status
@@ -342,3 +348,20 @@ def test_bench_sparse_work_count_equals_enumeration(S, nv, ns):
             for j in kt[act].tolist():
                 brute += rows * (rows + 1) // 2 if j == t else rows * 64
     assert bench.vs_active_pairs(w, vert, slash) == brute
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), api.DCA_E_DEVICE),                           # valid: reaches the first HIP call
+    (dict(q=0x50000000 + 4096), api.DCA_E_INVALID),       # q inside the workspace
+    (dict(v=0x50000000 + (1 << 20)), api.DCA_E_INVALID),  # v inside the workspace
+])
+def test_remap_rejects_inputs_inside_the_workspace(over, status):
+    if status == api.DCA_E_DEVICE and torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    sh = api.make_shape(1, 2, 1, 64, torch.float32)
+    args = dict(q=0x10000000, k=0x20000000, v=0x30000000, ws=0x50000000, ws_bytes=1 << 30)
+    args.update(over)
+    st = api.lib().dca_remap(args["q"], args["k"], args["v"], 2048, 512, 128, 1e7, 1.0, ctypes.byref(sh),
+                             args["ws"], args["ws_bytes"], None)
+    assert st == status
+    assert api.dca_last_error() != ""

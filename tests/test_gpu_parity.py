@@ -38,6 +38,8 @@ def _gpu():
     api.lib()
     yield
     torch.cuda.synchronize()
+    _ONE_M.clear()
+    torch.cuda.empty_cache()
 
 
 def _wl(name, **over):
@@ -259,23 +261,78 @@ def test_parity_sampled_rows(name):
     _discrimination(q, k, v, rows, w, ref, out[:, :, rows_t])
 
 
+# ---------------------------------------------------------------------------
+# the 1M-token Qwen2.5-14B shape (dense and vertical-slash), one seeded input
+# ---------------------------------------------------------------------------
+
+_ONE_M = {}
+
+
+def _one_m():
+    """The 1M-token Qwen2.5-14B workload at seed 0, shared by the 1M tests:
+    q, k, v on the device, k and v on the host, the 256 sampled rows (the
+    forced boundary rows plus seeded ones) and their queries on the host.
+    The dense and vertical-slash workloads draw the same q, k, v."""
+    if not _ONE_M:
+        w = workloads.get("qwen14b_1m")
+        q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+        rows = synth.sample_rows(w.seq, w.chunk, w.window, w.oracle_rows, seed=0)
+        _ONE_M.update(w=w, q=q, k=k, v=v, rows=rows, q_rows=q[:, :, torch.as_tensor(rows, device=DEV)].cpu(),
+                      kc=k.cpu(), vc=v.cpu())
+    return _ONE_M
+
+
+def _guard_subset(rows, C, n=48):
+    """Indices (into rows) of the rows the wrong-mapping guard re-runs the
+    oracle on: rows past the first chunk -- the only rows DCA changes --
+    every forced chunk and window boundary there plus evenly spread others,
+    n in all, so that the guard's extra oracle passes stay bounded."""
+    far = np.nonzero(rows >= C)[0]
+    pick = set(far[np.linspace(0, len(far) - 1, n).round().astype(int)].tolist())
+    boundary = {C, C + 1, 2 * C - 1, 2 * C, 3 * C, int(rows[-1])}
+    pick |= {int(i) for i in far if int(rows[i]) in boundary}
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def _oracle_host(m, idx, w, k=None, v=None, **kw):
+    rows = torch.as_tensor(m["rows"][idx])
+    return O.dca_prefill_rows(m["q_rows"][:, :, torch.as_tensor(idx)], rows, m["kc"] if k is None else k,
+                              m["vc"] if v is None else v, w.chunk, w.window, w.rope_base, w.yarn_scale, **kw)
+
+
 def test_parity_sampled_rows_1m():
     """The 1M-token Qwen2.5-14B shape in the launch configuration the
-    benchmark times: the oracle on the forced boundary rows plus seeded rows
-    (32 rows x 40 heads keeps the float64 oracle near half a minute)."""
-    w = workloads.get("qwen14b_1m")
-    rows = synth.sample_rows(w.seq, w.chunk, w.window, 32, seed=0)
+    benchmark times: the oracle on 256 seeded rows (the forced boundary rows
+    plus uniform ones) x 40 heads, out and lse within the bf16 bound; then the
+    discrimination guard on the rows past the first chunk: the GPU error there
+    must stay below a tenth of how far two wrong position mappings (vanilla
+    RoPE, and successive-chunk pairs treated as inter-chunk) move the oracle's
+    output, measured on a subset of 48 or more of those rows."""
+    m = _one_m()
+    w, rows = m["w"], m["rows"]
     say(f"[parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
-    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
-    out, lse = _run(q, k, v, w)
-    rows_t = torch.as_tensor(rows, device=DEV)
-    out_rows, lse_rows = out[:, :, rows_t].clone(), lse[:, :, rows_t].clone()
+    out, lse = _run(m["q"], m["k"], m["v"], w)
+    rows_d = torch.as_tensor(rows, device=DEV)
+    out_rows, lse_rows = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
     del out, lse
-    ref, ref_lse = _oracle(q, k, v, rows, w)
-    err, lerr = _err(out_rows, ref), _err(lse_rows, ref_lse)
+    torch.cuda.empty_cache()
+    ref, ref_lse = _oracle_host(m, np.arange(len(rows)), w)
+    m["dense_ref"] = ref
+    err, lerr = (out_rows - ref).abs().max().item(), (lse_rows - ref_lse).abs().max().item()
     say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
     assert err <= TOL["bf16"] and lerr <= 2e-2
-    _discrimination(q, k, v, rows, w, ref, out_rows)
+    far = torch.as_tensor(rows >= w.chunk)
+    err_far = (out_rows - ref)[:, :, far].abs().max().item()
+    g = _guard_subset(rows, w.chunk)
+    pqi, pqs, pin = O.query_positions(w.seq, w.chunk, w.window)
+    wrong_succ, _ = _oracle_host(m, g, w, query_pos=(pqi, torch.full_like(pqs, pin), pin))
+    van, _ = O.vanilla_prefill_rows(m["q_rows"][:, :, torch.as_tensor(g)], torch.as_tensor(rows[g]), m["kc"],
+                                    m["vc"], w.rope_base, w.yarn_scale)
+    d1 = (van - ref[:, :, torch.as_tensor(g)]).abs().max().item()
+    d2 = (wrong_succ - ref[:, :, torch.as_tensor(g)]).abs().max().item()
+    say(f"  rows >= C ({int(far.sum())}): gpu err={err_far:.3e}; wrong-mapping distances on {len(g)} of them: "
+        f"vanilla={d1:.3e} succ-as-inter={d2:.3e}; guard ratio err/min={err_far / min(d1, d2):.4f} (bound 0.1)")
+    assert err_far <= 0.1 * min(d1, d2)
 
 
 def test_fused_and_chunked_equal_whole_at_1m():
@@ -283,9 +340,9 @@ def test_fused_and_chunked_equal_whole_at_1m():
     benchmark times: the fused-rotation path and the chunked path (32 blocks
     of 32,768 rows) give the whole-sequence prefill's output and lse bit for
     bit (whose rows the oracle checks in the test above)."""
-    w = workloads.get("qwen14b_1m")
+    m = _one_m()
+    w, q, k, v = m["w"], m["q"], m["k"], m["v"]
     say(f"[1M] fused and chunked against the whole prefill, S={w.seq}")
-    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
     out, lse = _run(q, k, v, w)
     fout, flse = api.prefill(q, k, v, w.chunk, w.window, w.rope_base, w.yarn_scale, return_lse=True, fused=True)
     torch.cuda.synchronize()
@@ -319,21 +376,173 @@ def test_parity_4m_tokens():
 
 
 def test_vs_parity_1m():
-    """The 1M vertical-slash workload (1000 columns, 2000 offsets per head)
-    on sampled rows."""
+    """The 1M vertical-slash workload (1000 columns, 2000 offsets per head,
+    the dense workload's seed-0 inputs) on the same 256 sampled rows x 40
+    heads: out and lse within the bf16 bound, and two guards on the rows past
+    the first chunk, where outputs are small: the GPU error must stay below a
+    tenth of (a) the distance between the oracle's dense and sparse outputs
+    (a mask-ignoring or all-zero output fails it) and (b) how far treating
+    successive-chunk pairs as inter-chunk moves the sparse output."""
+    m = _one_m()
     w = workloads.get("qwen14b_1m_vs")
-    rows = synth.sample_rows(w.seq, w.chunk, w.window, 24, seed=1)
-    say(f"[vs parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
-    q, k, v = synth.make_qkv(w, seed=0, device=DEV)
+    rows = m["rows"]
     vert, slash = _vs_case(w, seed=0)
-    out, lse = _run(q, k, v, w, vertical=vert.to(DEV), slash=slash.to(DEV))
-    rows_t = torch.as_tensor(rows, device=DEV)
-    out_rows, lse_rows = out[:, :, rows_t].clone(), lse[:, :, rows_t].clone()
+    say(f"[vs parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
+    out, lse = _run(m["q"], m["k"], m["v"], w, vertical=vert.to(DEV), slash=slash.to(DEV))
+    rows_d = torch.as_tensor(rows, device=DEV)
+    out_rows, lse_rows = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
     del out, lse
-    ref, ref_lse = _oracle(q, k, v, rows, w, vertical=vert, slash=slash)
-    err, lerr = _err(out_rows, ref), _err(lse_rows, ref_lse)
+    torch.cuda.empty_cache()
+    ref, ref_lse = _oracle_host(m, np.arange(len(rows)), w, vertical=vert, slash=slash)
+    err, lerr = (out_rows - ref).abs().max().item(), (lse_rows - ref_lse).abs().max().item()
     say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
     assert err <= TOL["bf16"] and lerr <= 2e-2
+    dense = m.get("dense_ref")
+    if dense is None:
+        dense, _ = _oracle_host(m, np.arange(len(rows)), w)
+    far = torch.as_tensor(rows >= w.chunk)
+    err_far = (out_rows - ref)[:, :, far].abs().max().item()
+    dd = (dense - ref)[:, :, far].abs().max().item()
+    g = _guard_subset(rows, w.chunk)
+    pqi, pqs, pin = O.query_positions(w.seq, w.chunk, w.window)
+    wrong_succ, _ = _oracle_host(m, g, w, vertical=vert, slash=slash,
+                                 query_pos=(pqi, torch.full_like(pqs, pin), pin))
+    d2 = (wrong_succ - ref[:, :, torch.as_tensor(g)]).abs().max().item()
+    say(f"  rows >= C ({int(far.sum())}): gpu err={err_far:.3e}; dense-vs-sparse distance={dd:.3e} "
+        f"(ratio {err_far / dd:.4f}); succ-as-inter distance on {len(g)} rows={d2:.3e} "
+        f"(ratio {err_far / d2:.4f}); bound 0.1")
+    assert err_far <= 0.1 * dd
+    assert err_far <= 0.1 * d2
+
+
+def _needle_key(q_row, qpos, kpos, w):
+    """A key that, rotated to position kpos, is a multiple of the query row
+    rotated to qpos, scaled so that the pair's logit is 20: the needle then
+    takes almost all of the row's softmax weight (about 0.998 against a
+    million keys of these inputs) under the right position map only."""
+    rq = O.rope_rotate(q_row.reshape(1, -1), torch.tensor([int(qpos)]), w.rope_base)
+    alpha = 20.0 / (w.yarn_scale * rq.norm().item() ** 2 / math.sqrt(w.head_dim))
+    return O.rope_rotate(alpha * rq, torch.tensor([-int(kpos)]), w.rope_base)[0]
+
+
+def _plant(m, w, cases, h=0):
+    """k with one needle key per case (row i, key j, query position of the
+    pair's region) for query head h, on the device and (KV head of h only)
+    on the host."""
+    kvh = h // (w.n_q_heads // w.n_kv_heads)
+    k2 = m["k"].clone()
+    kh = m["kc"][:, kvh:kvh + 1].clone()
+    pk = O.key_positions(w.seq, w.chunk)
+    for i, j, qpos in cases:
+        key = _needle_key(m["q"][0, h, i].cpu(), qpos, pk[j], w).to(m["k"].dtype)
+        k2[0, kvh, j] = key.to(DEV)
+        kh[0, 0, j] = key
+    return k2, kh
+
+
+def _oracle_group(m, w, rows, kh, h=0, **kw):
+    """The oracle on a few rows of the query heads sharing h's KV head."""
+    G = w.n_q_heads // w.n_kv_heads
+    kvh = h // G
+    rows_t = torch.as_tensor(rows)
+    qg = m["q"][:, kvh * G:(kvh + 1) * G][:, :, rows_t.to(DEV)].cpu()
+    vh = m["vc"][:, kvh:kvh + 1]
+    if "vertical" in kw:
+        kw = {**kw, "vertical": kw["vertical"][kvh * G:(kvh + 1) * G], "slash": kw["slash"][kvh * G:(kvh + 1) * G]}
+    return O.dca_prefill_rows(qg, rows_t, kh, vh, w.chunk, w.window, w.rope_base, w.yarn_scale, **kw)
+
+
+def test_planted_needles_1m():
+    """Planted needles at the 1M-token shape, one per region: a successive
+    pair inside the local window (true distance), a successive pair past it
+    (pinned query), an inter-chunk pair and an intra-chunk pair. Each needle
+    row's output must be within 0.06 of the needle's value row; a wrong query
+    variant turns the needle away and leaves the row near the mean of a
+    million values (far from it). The rows of the KV group's five heads are
+    checked against the oracle as well."""
+    m = _one_m()
+    w = m["w"]
+    S, C, W = w.seq, w.chunk, w.window
+    pqi, pqs, pin = O.query_positions(S, C, W)
+    cases = [  # (row, key, query position of the pair's region)
+        (C + 3, C - 5, int(pqs[C + 3])),                           # successive, inside the window
+        (2 * C + W + 10, C + 7, int(pqs[2 * C + W + 10])),         # successive, pinned
+        (3 * C + 5, 100, pin),                                     # inter
+        (2 * C + 500, 2 * C + 200, int(pqi[2 * C + 500])),         # intra
+    ]
+    say(f"[needles 1M] S={S} C={C} W={W}: rows {[c[0] for c in cases]}")
+    k2, kh = _plant(m, w, cases)
+    out, _ = _run(m["q"], k2, m["v"], w)
+    rows = np.array([c[0] for c in cases])
+    got = out[:, :5, torch.as_tensor(rows, device=DEV)].double().cpu()
+    del out, k2
+    torch.cuda.empty_cache()
+    ref, _ = _oracle_group(m, w, rows, kh)
+    for n, (i, j, _) in enumerate(cases):
+        target = m["vc"][0, 0, j].double()
+        dg, do = (got[0, 0, n] - target).abs().max().item(), (ref[0, 0, n] - target).abs().max().item()
+        say(f"  row {i} key {j}: |gpu - v_j|={dg:.3e} |oracle - v_j|={do:.3e}")
+        assert do < 0.05 and dg < 0.06
+    err = (got - ref).abs().max().item()
+    say(f"  five heads of the group on the needle rows: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_vs_needles_1m():
+    """Needles under the 1M vertical-slash mask (head 0's lists): one key in
+    a tile active through a vertical column (inter-chunk pair) and one in a
+    tile active through a slash distance (successive pair inside the window)
+    must each dominate their row; one in a tile the mask leaves out
+    (successive pair, pinned query) must not move its row at all: that row is
+    bit-identical to the sparse prefill without the needles, and far from the
+    needle's value row (where a dense, mask-ignoring kernel would put it)."""
+    m = _one_m()
+    w = workloads.get("qwen14b_1m_vs")
+    S, C, W = w.seq, w.chunk, w.window
+    vert, slash = _vs_case(w, seed=0)
+    vt, dl = O.vs_tile_lists(vert[0], slash[0], S)
+    vt_set, dl_set = set(vt.tolist()), set(dl.tolist())
+    pqs, pin = O.query_positions(S, C, W)[1:]
+    tpc = C // 64
+    i_a = 3 * C + 5                                   # inter: key tile with a vertical column, chunk 0
+    kt_a = next(int(t) for t in vt.tolist() if 4 <= t < tpc - 4)
+    i_s = C + 3                                       # successive inside the window: slash-active tile of chunk 0
+    t_s = i_s // 64
+    kt_s = next(t_s - d for d in sorted(dl_set, reverse=True) if 0 < t_s - d < tpc - 1 and t_s - d not in vt_set
+                and t_s - d != kt_a)
+    i_n = 2 * C + W + 10                              # successive, pinned: an inactive tile of chunk 1
+    t_n = i_n // 64
+    kt_n = next(kt for kt in range(tpc + 8, 2 * tpc - 8) if kt not in vt_set and t_n - kt not in dl_set)
+    cases = [(i_a, 64 * kt_a + 7, pin), (i_s, 64 * kt_s + 9, int(pqs[i_s])), (i_n, 64 * kt_n + 11, int(pqs[i_n]))]
+    for i, j, _ in cases:
+        say(f"[vs needles 1M] row {i} key {j}: tile ({i // 64}, {j // 64}) "
+            f"active={bool(O.vs_tile_active(vert[0], slash[0], torch.tensor([i // 64]), torch.tensor([j // 64]))[0])}")
+    vd, sd = vert.to(DEV), slash.to(DEV)
+    rows = np.array([c[0] for c in cases])
+    rows_d = torch.as_tensor(rows, device=DEV)
+    base, _ = _run(m["q"], m["k"], m["v"], w, vertical=vd, slash=sd)
+    base_rows = base[:, :5, rows_d].clone()
+    del base
+    k2, kh = _plant(m, w, cases)
+    out, _ = _run(m["q"], k2, m["v"], w, vertical=vd, slash=sd)
+    got_dev = out[:, :5, rows_d].clone()
+    del out, k2
+    torch.cuda.empty_cache()
+    got = got_dev.double().cpu()
+    ref, _ = _oracle_group(m, w, rows, kh, vertical=vert, slash=slash)
+    for n, (i, j, _) in enumerate(cases[:2]):
+        target = m["vc"][0, 0, j].double()
+        dg, do = (got[0, 0, n] - target).abs().max().item(), (ref[0, 0, n] - target).abs().max().item()
+        say(f"  active: row {i} key {j}: |gpu - v_j|={dg:.3e} |oracle - v_j|={do:.3e}")
+        assert do < 0.05 and dg < 0.06
+    i, j, _ = cases[2]
+    far = (got[0, 0, 2] - m["vc"][0, 0, j].double()).abs().max().item()
+    same = torch.equal(got_dev[0, 0, 2], base_rows[0, 0, 2])
+    say(f"  inactive: row {i} key {j}: identical to the prefill without needles: {same}; |gpu - v_j|={far:.3e}")
+    assert same and far > 0.2
+    err = (got - ref).abs().max().item()
+    say(f"  five heads of the group on the needle rows: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 def test_planted_needles_bf16():
