@@ -294,43 +294,69 @@ def _guard_subset(rows, C, n=48):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-def _oracle_host(m, idx, w, k=None, v=None, **kw):
-    rows = torch.as_tensor(m["rows"][idx])
-    return O.dca_prefill_rows(m["q_rows"][:, :, torch.as_tensor(idx)], rows, m["kc"] if k is None else k,
-                              m["vc"] if v is None else v, w.chunk, w.window, w.rope_base, w.yarn_scale, **kw)
+def _group_args(m, w, g, idx):
+    """Host tensors of KV group g: its query heads' sampled rows idx, its keys
+    and values (the oracle's definition restricted to one KV group)."""
+    G = w.n_q_heads // w.n_kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    return hs, m["q_rows"][:, hs][:, :, torch.as_tensor(idx)], m["kc"][:, g:g + 1], m["vc"][:, g:g + 1]
 
 
-def test_parity_sampled_rows_1m():
-    """The 1M-token Qwen2.5-14B shape in the launch configuration the
-    benchmark times: the oracle on 256 seeded rows (the forced boundary rows
-    plus uniform ones) x 40 heads, out and lse within the bf16 bound; then the
-    discrimination guard on the rows past the first chunk: the GPU error there
-    must stay below a tenth of how far two wrong position mappings (vanilla
-    RoPE, and successive-chunk pairs treated as inter-chunk) move the oracle's
-    output, measured on a subset of 48 or more of those rows."""
+def _oracle_group_rows(m, w, g, idx, **kw):
+    hs, qg, kg, vg = _group_args(m, w, g, idx)
+    if kw.get("vertical") is not None:
+        kw = {**kw, "vertical": kw["vertical"][hs], "slash": kw["slash"][hs]}
+    return O.dca_prefill_rows(qg, torch.as_tensor(m["rows"][idx]), kg, vg, w.chunk, w.window, w.rope_base,
+                              w.yarn_scale, **kw)
+
+
+def test_prefill_1m_dense():
+    """The 1M-token Qwen2.5-14B prefill in the launch configuration the
+    benchmark times; its 256 sampled rows (forced boundary rows plus seeded
+    ones) are kept for the per-group oracle checks that follow."""
     m = _one_m()
-    w, rows = m["w"], m["rows"]
-    say(f"[parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
+    w = m["w"]
+    say(f"[parity 1M] prefill S={w.seq}; {len(m['rows'])} sampled rows x {w.n_q_heads} heads kept")
     out, lse = _run(m["q"], m["k"], m["v"], w)
-    rows_d = torch.as_tensor(rows, device=DEV)
-    out_rows, lse_rows = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
+    rows_d = torch.as_tensor(m["rows"], device=DEV)
+    m["dense_out"], m["dense_lse"] = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
     del out, lse
     torch.cuda.empty_cache()
-    ref, ref_lse = _oracle_host(m, np.arange(len(rows)), w)
-    m["dense_ref"] = ref
-    err, lerr = (out_rows - ref).abs().max().item(), (lse_rows - ref_lse).abs().max().item()
+    assert torch.isfinite(m["dense_out"]).all()
+
+
+@pytest.mark.parametrize("g", range(8))
+def test_parity_1m_dense_group(g):
+    """One KV group (5 query heads) of the 1M prefill against the oracle on
+    the 256 sampled rows: out and lse within the bf16 bound. Then the
+    discrimination guard on the rows past the first chunk, the only rows DCA
+    changes: the GPU error there must stay below a tenth of how far two wrong
+    position mappings (vanilla RoPE, and successive-chunk pairs treated as
+    inter-chunk) move the oracle's output, those distances measured on 48 or
+    more of those rows including every chunk boundary among them."""
+    m = _one_m()
+    if "dense_out" not in m:
+        pytest.skip("needs test_prefill_1m_dense")
+    w, rows = m["w"], m["rows"]
+    G = w.n_q_heads // w.n_kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    say(f"[parity 1M] KV group {g}: oracle on {len(rows)} rows x {G} heads")
+    ref, ref_lse = _oracle_group_rows(m, w, g, np.arange(len(rows)))
+    m.setdefault("dense_ref", {})[g] = ref
+    got, got_lse = m["dense_out"][:, hs], m["dense_lse"][:, hs]
+    err, lerr = (got - ref).abs().max().item(), (got_lse - ref_lse).abs().max().item()
     say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
     assert err <= TOL["bf16"] and lerr <= 2e-2
     far = torch.as_tensor(rows >= w.chunk)
-    err_far = (out_rows - ref)[:, :, far].abs().max().item()
-    g = _guard_subset(rows, w.chunk)
+    err_far = (got - ref)[:, :, far].abs().max().item()
+    gi = _guard_subset(rows, w.chunk)
     pqi, pqs, pin = O.query_positions(w.seq, w.chunk, w.window)
-    wrong_succ, _ = _oracle_host(m, g, w, query_pos=(pqi, torch.full_like(pqs, pin), pin))
-    van, _ = O.vanilla_prefill_rows(m["q_rows"][:, :, torch.as_tensor(g)], torch.as_tensor(rows[g]), m["kc"],
-                                    m["vc"], w.rope_base, w.yarn_scale)
-    d1 = (van - ref[:, :, torch.as_tensor(g)]).abs().max().item()
-    d2 = (wrong_succ - ref[:, :, torch.as_tensor(g)]).abs().max().item()
-    say(f"  rows >= C ({int(far.sum())}): gpu err={err_far:.3e}; wrong-mapping distances on {len(g)} of them: "
+    wrong_succ, _ = _oracle_group_rows(m, w, g, gi, query_pos=(pqi, torch.full_like(pqs, pin), pin))
+    _, qg, kg, vg = _group_args(m, w, g, gi)
+    van, _ = O.vanilla_prefill_rows(qg, torch.as_tensor(rows[gi]), kg, vg, w.rope_base, w.yarn_scale)
+    ref_g = ref[:, :, torch.as_tensor(gi)]
+    d1, d2 = (van - ref_g).abs().max().item(), (wrong_succ - ref_g).abs().max().item()
+    say(f"  rows >= C ({int(far.sum())}): gpu err={err_far:.3e}; wrong-mapping distances on {len(gi)} of them: "
         f"vanilla={d1:.3e} succ-as-inter={d2:.3e}; guard ratio err/min={err_far / min(d1, d2):.4f} (bound 0.1)")
     assert err_far <= 0.1 * min(d1, d2)
 
@@ -375,41 +401,58 @@ def test_parity_4m_tokens():
     _discrimination(q, k, v, rows, w, ref, out_rows)
 
 
-def test_vs_parity_1m():
+def test_prefill_1m_vertical_slash():
     """The 1M vertical-slash workload (1000 columns, 2000 offsets per head,
-    the dense workload's seed-0 inputs) on the same 256 sampled rows x 40
-    heads: out and lse within the bf16 bound, and two guards on the rows past
-    the first chunk, where outputs are small: the GPU error must stay below a
-    tenth of (a) the distance between the oracle's dense and sparse outputs
-    (a mask-ignoring or all-zero output fails it) and (b) how far treating
-    successive-chunk pairs as inter-chunk moves the sparse output."""
+    the dense workload's seed-0 inputs); its 256 sampled rows are kept for
+    the per-group checks that follow."""
     m = _one_m()
     w = workloads.get("qwen14b_1m_vs")
-    rows = m["rows"]
     vert, slash = _vs_case(w, seed=0)
-    say(f"[vs parity 1M] {len(rows)} sampled rows x {w.n_q_heads} heads")
+    m["vert"], m["slash"] = vert, slash
+    say(f"[vs parity 1M] prefill S={w.seq}, {w.n_vertical} columns and {w.n_slash} offsets per head")
     out, lse = _run(m["q"], m["k"], m["v"], w, vertical=vert.to(DEV), slash=slash.to(DEV))
-    rows_d = torch.as_tensor(rows, device=DEV)
-    out_rows, lse_rows = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
+    rows_d = torch.as_tensor(m["rows"], device=DEV)
+    m["vs_out"], m["vs_lse"] = out[:, :, rows_d].double().cpu(), lse[:, :, rows_d].double().cpu()
     del out, lse
     torch.cuda.empty_cache()
-    ref, ref_lse = _oracle_host(m, np.arange(len(rows)), w, vertical=vert, slash=slash)
-    err, lerr = (out_rows - ref).abs().max().item(), (lse_rows - ref_lse).abs().max().item()
+    assert torch.isfinite(m["vs_out"]).all()
+
+
+@pytest.mark.parametrize("g", range(8))
+def test_vs_parity_1m_group(g):
+    """One KV group of the 1M vertical-slash prefill against the oracle on
+    the 256 sampled rows: out and lse within the bf16 bound, and two guards
+    on the rows past the first chunk, where outputs are small: the GPU error
+    must stay below a tenth of (a) the distance between the oracle's dense
+    and sparse outputs (a mask-ignoring or all-zero output fails it) and (b)
+    how far treating successive-chunk pairs as inter-chunk moves the sparse
+    output (on 48 or more of those rows)."""
+    m = _one_m()
+    if "vs_out" not in m:
+        pytest.skip("needs test_prefill_1m_vertical_slash")
+    w = workloads.get("qwen14b_1m_vs")
+    rows, vert, slash = m["rows"], m["vert"], m["slash"]
+    G = w.n_q_heads // w.n_kv_heads
+    hs = slice(g * G, (g + 1) * G)
+    say(f"[vs parity 1M] KV group {g}: oracle on {len(rows)} rows x {G} heads")
+    ref, ref_lse = _oracle_group_rows(m, w, g, np.arange(len(rows)), vertical=vert, slash=slash)
+    got, got_lse = m["vs_out"][:, hs], m["vs_lse"][:, hs]
+    err, lerr = (got - ref).abs().max().item(), (got_lse - ref_lse).abs().max().item()
     say(f"  max abs err out={err:.3e} lse={lerr:.3e}")
     assert err <= TOL["bf16"] and lerr <= 2e-2
-    dense = m.get("dense_ref")
+    dense = m.get("dense_ref", {}).get(g)
     if dense is None:
-        dense, _ = _oracle_host(m, np.arange(len(rows)), w)
+        dense, _ = _oracle_group_rows(m, w, g, np.arange(len(rows)))
     far = torch.as_tensor(rows >= w.chunk)
-    err_far = (out_rows - ref)[:, :, far].abs().max().item()
+    err_far = (got - ref)[:, :, far].abs().max().item()
     dd = (dense - ref)[:, :, far].abs().max().item()
-    g = _guard_subset(rows, w.chunk)
+    gi = _guard_subset(rows, w.chunk)
     pqi, pqs, pin = O.query_positions(w.seq, w.chunk, w.window)
-    wrong_succ, _ = _oracle_host(m, g, w, vertical=vert, slash=slash,
-                                 query_pos=(pqi, torch.full_like(pqs, pin), pin))
-    d2 = (wrong_succ - ref[:, :, torch.as_tensor(g)]).abs().max().item()
+    wrong_succ, _ = _oracle_group_rows(m, w, g, gi, vertical=vert, slash=slash,
+                                       query_pos=(pqi, torch.full_like(pqs, pin), pin))
+    d2 = (wrong_succ - ref[:, :, torch.as_tensor(gi)]).abs().max().item()
     say(f"  rows >= C ({int(far.sum())}): gpu err={err_far:.3e}; dense-vs-sparse distance={dd:.3e} "
-        f"(ratio {err_far / dd:.4f}); succ-as-inter distance on {len(g)} rows={d2:.3e} "
+        f"(ratio {err_far / dd:.4f}); succ-as-inter distance on {len(gi)} rows={d2:.3e} "
         f"(ratio {err_far / d2:.4f}); bound 0.1")
     assert err_far <= 0.1 * dd
     assert err_far <= 0.1 * d2
@@ -518,31 +561,38 @@ def test_vs_needles_1m():
         say(f"[vs needles 1M] row {i} key {j}: tile ({i // 64}, {j // 64}) "
             f"active={bool(O.vs_tile_active(vert[0], slash[0], torch.tensor([i // 64]), torch.tensor([j // 64]))[0])}")
     vd, sd = vert.to(DEV), slash.to(DEV)
-    rows = np.array([c[0] for c in cases])
-    rows_d = torch.as_tensor(rows, device=DEV)
-    base, _ = _run(m["q"], m["k"], m["v"], w, vertical=vd, slash=sd)
-    base_rows = base[:, :5, rows_d].clone()
-    del base
-    k2, kh = _plant(m, w, cases)
+    G = w.n_q_heads // w.n_kv_heads
+    # the two active needles together; the inactive one alone (a vertical
+    # needle is visible to every later query tile, the inactive row's too)
+    active, inactive = cases[:2], cases[2:]
+    rows = np.array([c[0] for c in active])
+    k2, kh = _plant(m, w, active)
     out, _ = _run(m["q"], k2, m["v"], w, vertical=vd, slash=sd)
-    got_dev = out[:, :5, rows_d].clone()
+    got = out[:, :G, torch.as_tensor(rows, device=DEV)].double().cpu()
     del out, k2
     torch.cuda.empty_cache()
-    got = got_dev.double().cpu()
     ref, _ = _oracle_group(m, w, rows, kh, vertical=vert, slash=slash)
-    for n, (i, j, _) in enumerate(cases[:2]):
+    for n, (i, j, _) in enumerate(active):
         target = m["vc"][0, 0, j].double()
         dg, do = (got[0, 0, n] - target).abs().max().item(), (ref[0, 0, n] - target).abs().max().item()
         say(f"  active: row {i} key {j}: |gpu - v_j|={dg:.3e} |oracle - v_j|={do:.3e}")
         assert do < 0.05 and dg < 0.06
-    i, j, _ = cases[2]
-    far = (got[0, 0, 2] - m["vc"][0, 0, j].double()).abs().max().item()
-    same = torch.equal(got_dev[0, 0, 2], base_rows[0, 0, 2])
-    say(f"  inactive: row {i} key {j}: identical to the prefill without needles: {same}; |gpu - v_j|={far:.3e}")
-    assert same and far > 0.2
     err = (got - ref).abs().max().item()
-    say(f"  five heads of the group on the needle rows: max abs err {err:.3e}")
+    say(f"  {G} heads of the group on the active needles' rows: max abs err {err:.3e}")
     assert err <= TOL["bf16"]
+    i, j, _ = inactive[0]
+    base, _ = _run(m["q"], m["k"], m["v"], w, vertical=vd, slash=sd)
+    base_row = base[0, 0, i].clone()
+    del base
+    k3, _ = _plant(m, w, inactive)
+    out, _ = _run(m["q"], k3, m["v"], w, vertical=vd, slash=sd)
+    got_row = out[0, 0, i].clone()
+    del out, k3
+    torch.cuda.empty_cache()
+    far = (got_row.double().cpu() - m["vc"][0, 0, j].double()).abs().max().item()
+    same = torch.equal(got_row, base_row)
+    say(f"  inactive: row {i} key {j}: identical to the prefill without the needle: {same}; |gpu - v_j|={far:.3e}")
+    assert same and far > 0.2
 
 
 def test_planted_needles_bf16():
