@@ -225,6 +225,30 @@ int dca_decode(const void *q, const void *k, const void *v, void *out, float *ls
                float yarn_scale, const dca_shape *shape, void *workspace,
                size_t workspace_bytes, void *stream);
 
+/* dca_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments and errors as dca_decode, and outputs
+ * identical to it, but the scratch of the split-key reduction (the rotated
+ * query variants and the per-split partial results: batch * n_q_heads *
+ * (3 * head_dim * element size, rounded up to 256 bytes, + 256 *
+ * (head_dim + 2) * 4) bytes) lives in a static device array of
+ * DCA_DECODE_STATIC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends, instead of in the workspace. The
+ * workspace then only needs the key/value cache: any workspace for this
+ * sequence from dca_fused_workspace_size, dca_workspace_size or
+ * dca_chunk_workspace_size (mask NULL). A call whose scratch exceeds the
+ * array returns DCA_E_UNSUPPORTED and enqueues nothing. The first call on a
+ * device looks up the array's address there (a HIP call, no allocation); no
+ * call allocates or frees memory. Every call on one GPU shares that GPU's
+ * array, whose contents the last call left (nothing in it needs to start at
+ * zero): calls that overlap in time on one GPU -- on different streams or
+ * host threads -- race on it and must not be made. */
+#define DCA_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int dca_decode_static(const void *q, const void *k, const void *v, void *out, float *lse,
+                      int64_t pos, int64_t seq, int64_t C, int64_t W, double rope_base,
+                      float yarn_scale, const dca_shape *shape, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* The three stages of dca_prefill, callable one at a time on the same
  * workspace (for per-stage timing and checks):
  *   dca_remap      -- the RoPE/DCA pre-pass: writes the cos/sin table, the

@@ -22,7 +22,7 @@ DCA_F32, DCA_BF16 = 0, 1
 EXPORTS = [
     "dca_status_str", "dca_last_error", "dca_remap_positions", "dca_workspace_size",
     "dca_prefill", "dca_remap", "dca_vs_index", "dca_attention",
-    "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode", "dca_fused_workspace_size",
+    "dca_chunk_workspace_size", "dca_prefill_chunk", "dca_decode", "dca_decode_static", "dca_fused_workspace_size",
     "dca_prefill_fused", "dca_vs_estimate_workspace_size", "dca_vs_estimate",
     "dca_debug_positions", "dca_debug_tile_regions", "dca_debug_unpack", "dca_debug_vs_lists",
     "dca_debug_vs_tiles",
@@ -71,6 +71,8 @@ _SIGS = {
                                        _VP, ctypes.c_size_t, _VP]),
     "dca_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_float,
                                   _VP, _VP, ctypes.c_size_t, _VP]),
+    "dca_decode_static": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_double,
+                                         ctypes.c_float, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_attention": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "dca_debug_positions": (ctypes.c_int, [_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "dca_debug_tile_regions": (ctypes.c_int, [_I64, _I64, _VP, _VP]),
@@ -262,6 +264,13 @@ def dca_decode(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, 
                stream=None):
     _check(lib().dca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pos, seq, C, W, rope_base, yarn_scale,
                             ctypes.byref(shape), _ptr(workspace), workspace_bytes, _stream(stream)), "dca_decode")
+
+
+def dca_decode_static(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
+                      stream=None):
+    _check(lib().dca_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), pos, seq, C, W, rope_base,
+                                   yarn_scale, ctypes.byref(shape), _ptr(workspace), workspace_bytes,
+                                   _stream(stream)), "dca_decode_static")
 
 
 def dca_debug_positions(seq, C, W, pq_intra, pq_succ, pq_inter, pk, stream=None):

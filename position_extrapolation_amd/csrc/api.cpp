@@ -472,9 +472,14 @@ int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, d
     return ok();
 }
 
-int dca_decode(const void *q, const void *k, const void *v, void *out, float *lse, int64_t pos, int64_t seq,
-               int64_t C, int64_t W, double rope_base, float yarn_scale, const dca_shape *shape, void *workspace,
-               size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+// dca_decode and dca_decode_static: the same checks and launches; the scratch
+// of the split-key reduction lives in the workspace's query section, or
+// (static_scratch) in the library's static device array.
+static int decode_call(const void *q, const void *k, const void *v, void *out, float *lse, int64_t pos,
+                       int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale, const dca_shape *shape,
+                       void *workspace, size_t workspace_bytes, void *stream, bool static_scratch) {
     Problem p;
     Layout L;
     int st = make_problem(seq, C, W, shape, nullptr, &p);
@@ -486,20 +491,51 @@ int dca_decode(const void *q, const void *k, const void *v, void *out, float *ls
     p.q0 = pos;
     p.NQ = 1;
     p.NQ_pad = kSeqPad;
+    // with the static scratch the workspace needs the key/value cache only
+    p.fused = static_scratch;
     if (q == nullptr || k == nullptr || v == nullptr) return fail(DCA_E_INVALID, "q, k and v must be non-NULL");
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
         return fail(DCA_E_INVALID, "q, k and v must be 16-byte aligned");
     if ((st = check_rope(rope_base))) return st;
     if ((st = check_yarn(yarn_scale))) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
-    if (decode_scratch_bytes(p) > L.total - L.q[0])
+    if (static_scratch) {
+        if (decode_scratch_bytes(p) > kDecodeStaticScratchBytes)
+            return fail(DCA_E_UNSUPPORTED,
+                        "the decode scratch of batch %lld x %lld query heads (d = %lld) needs %zu bytes; the static "
+                        "array holds %zu (use dca_decode with a workspace)",
+                        (long long)p.B, (long long)p.Hq, (long long)p.D, decode_scratch_bytes(p),
+                        kDecodeStaticScratchBytes);
+    } else if (decode_scratch_bytes(p) > L.total - L.q[0]) {
         return fail(DCA_E_WORKSPACE, "query section too small for the decode scratch");
+    }
     const void *inputs[3] = {q, k, v};
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    void *scratch_base = nullptr;
+    if (static_scratch) {
+        const int err = decode_static_scratch(&scratch_base);
+        if (err) return device_fail(err, "static scratch lookup");
+    }
     const float k_scale = yarn_scale * p.softmax_scale * 1.4426950408889634f;
-    const int err = launch_decode(p, q, k, v, out, lse, rope_base, k_scale, workspace, L, stream);
+    const int err = launch_decode(p, q, k, v, out, lse, rope_base, k_scale, workspace, L, stream, scratch_base);
     if (err) return device_fail(err, "decode launch");
     return ok();
+}
+
+extern "C" {
+
+int dca_decode(const void *q, const void *k, const void *v, void *out, float *lse, int64_t pos, int64_t seq,
+               int64_t C, int64_t W, double rope_base, float yarn_scale, const dca_shape *shape, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    return decode_call(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
+                       stream, false);
+}
+
+int dca_decode_static(const void *q, const void *k, const void *v, void *out, float *lse, int64_t pos, int64_t seq,
+                      int64_t C, int64_t W, double rope_base, float yarn_scale, const dca_shape *shape,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_call(q, k, v, out, lse, pos, seq, C, W, rope_base, yarn_scale, shape, workspace, workspace_bytes,
+                       stream, true);
 }
 
 int dca_debug_positions(int64_t seq, int64_t C, int64_t W, int32_t *pq_intra, int32_t *pq_succ,

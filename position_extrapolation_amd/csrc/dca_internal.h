@@ -108,10 +108,17 @@ int launch_vs_index(const Problem &p, const dca_vs_mask &m, void *ws, const Layo
 // q_nat != null: fused rotation, the kernel turns the caller's queries itself
 int launch_attention(const Problem &p, void *out, float *lse, const void *ws, const Layout &L, void *stream,
                      const void *q_nat = nullptr);
-// decode of the token at index p.q0 (p.NQ = 1); scratch lives in the query section
+// decode of the token at index p.q0 (p.NQ = 1); its scratch (query variants and
+// split partials, decode_scratch_bytes) lives in the workspace's query section,
+// or at scratch_base when that is not null
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
-                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream);
+                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream,
+                  void *scratch_base = nullptr);
 size_t decode_scratch_bytes(const Problem &p);
+// the static device array that holds the decode scratch for dca_decode_static:
+// its size, and its address on the current device (looked up once per device)
+constexpr size_t kDecodeStaticScratchBytes = DCA_DECODE_STATIC_SCRATCH_BYTES;
+int decode_static_scratch(void **ptr);
 // online vertical-slash estimation over the keys rotated at their own index
 // (the pre-pass run with C >= S, W = 0, keys only)
 size_t est_scratch_bytes(const Problem &p);

@@ -24,6 +24,8 @@
 // The attention launch is bound by HBM: it reads the cache once.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dca_internal.h"
 #include "frag.h"
 #include "tile_math.h"
@@ -278,16 +280,18 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
 
 template <typename T, int D>
 static int launch_decode_t(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
-                           double rope_base, float k_scale, void *ws, const Layout &L, void *stream) {
+                           double rope_base, float k_scale, void *ws, const Layout &L, void *scratch_base,
+                           void *stream) {
     DecodeArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
     a.kf = (char *)ws + L.k;
     a.vf = (char *)ws + L.v;
-    a.qv = (char *)ws + L.q[0];
+    char *sbase = scratch_base != nullptr ? (char *)scratch_base : (char *)ws + L.q[0];
+    a.qv = sbase;
     const size_t qv_bytes = ((size_t)p.B * p.Hq * 3 * D * sizeof(T) + 255) & ~(size_t)255;
-    a.part = (float *)((char *)ws + L.q[0] + qv_bytes);
+    a.part = (float *)(sbase + qv_bytes);
     a.out = out;
     a.lse = lse;
     for (int m = 0; m < D / 2; ++m) a.th.theta[m] = pow(rope_base, -2.0 * m / (double)D);
@@ -324,12 +328,47 @@ size_t decode_scratch_bytes(const Problem &p) {
 }
 
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
-                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream) {
+                  double rope_base, float k_scale, void *ws, const Layout &L, void *stream, void *scratch_base) {
     if (p.dtype == DCA_BF16)
-        return p.D == 128 ? launch_decode_t<__bf16, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream)
-                          : launch_decode_t<__bf16, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream);
-    return p.D == 128 ? launch_decode_t<float, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream)
-                      : launch_decode_t<float, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, stream);
+        return p.D == 128
+                   ? launch_decode_t<__bf16, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, scratch_base, stream)
+                   : launch_decode_t<__bf16, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, scratch_base, stream);
+    return p.D == 128
+               ? launch_decode_t<float, 128>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, scratch_base, stream)
+               : launch_decode_t<float, 64>(p, q, k, v, out, lse, rope_base, k_scale, ws, L, scratch_base, stream);
+}
+
+// ---------------------------------------------------------------------------
+// the decode scratch in a static device array (dca_decode_static)
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate: the rotated query variants and the
+// split partials live here instead of in the workspace's query section.
+// Every GPU the library runs on holds its own copy, at its own address, until
+// the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: only the address hipGetSymbolAddress returns for the
+// current device may reach a kernel.
+static __device__ __align__(256) char scratch[kDecodeStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+int decode_static_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // once per device, with that device current
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (addr == nullptr) return (int)hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = addr;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
 }
 
 }  // namespace dca

@@ -365,3 +365,40 @@ def test_remap_rejects_inputs_inside_the_workspace(over, status):
                              args["ws"], args["ws_bytes"], None)
     assert st == status
     assert api.dca_last_error() != ""
+
+
+def _call_decode_static(**over):
+    sh = over.pop("shape", api.make_shape(1, 4, 2, 64, torch.float32))
+    args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, pos=700, seq=2048, C=512,
+                W=128, base=1e7, yarn=1.0, ws=0x50000000, ws_bytes=None)
+    args.update(over)
+    if args["ws_bytes"] is None:     # the key/value cache alone
+        args["ws_bytes"] = api.dca_fused_workspace_size(args["seq"], args["C"], args["W"], sh)
+    return api.lib().dca_decode_static(args["q"], args["k"], args["v"], args["out"], args["lse"], args["pos"],
+                                       args["seq"], args["C"], args["W"], args["base"], args["yarn"],
+                                       ctypes.byref(sh), args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(pos=2048), api.DCA_E_INVALID),
+    (dict(q=None), api.DCA_E_INVALID),
+    (dict(ws_bytes=1 << 12), api.DCA_E_WORKSPACE),         # smaller than the key/value cache
+    (dict(out=0x10000000), api.DCA_E_INVALID),             # out aliases q
+    # 4 x 64 query heads of d = 128: about 34 MB of scratch, past the 16 MiB array
+    (dict(shape=api.make_shape(4, 64, 8, 128, torch.bfloat16)), api.DCA_E_UNSUPPORTED),
+])
+def test_decode_static_arguments_rejected_before_any_hip_call(over, status):
+    assert _call_decode_static(**over) == status
+    assert api.dca_last_error() != ""
+
+
+def test_decode_static_takes_a_cache_only_workspace():
+    """Without a GPU a valid call reaches the scratch lookup (the first HIP
+    call) and reports DCA_E_DEVICE; dca_decode rejects the same workspace,
+    which has no room for its scratch."""
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_decode_static() == api.DCA_E_DEVICE
+    sh = api.make_shape(1, 4, 2, 64, torch.float32)
+    nb = api.dca_fused_workspace_size(2048, 512, 128, sh)
+    assert _call_decode(ws_bytes=nb) == api.DCA_E_WORKSPACE
