@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdca.so")
+# DCA_LIBRARY names another build of the same library (the host-only
+# sanitizer build the CPU tests make); the default is the in-tree libdca.so
+LIB_PATH = os.environ.get("DCA_LIBRARY") or os.path.join(_PKG, "libdca.so")
 
 DCA_OK, DCA_E_INVALID, DCA_E_UNSUPPORTED, DCA_E_WORKSPACE, DCA_E_DEVICE = range(5)
 DCA_F32, DCA_BF16 = 0, 1

@@ -38,6 +38,21 @@ const char *hip_error_text(int err) { return hipGetErrorString((hipError_t)err);
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Scratch sizes of the decode and the vertical-slash estimate (host
+// arithmetic; the kernels take the same offsets).
+size_t decode_scratch_bytes(const Problem &p) {
+    const size_t qv = align256((size_t)p.B * p.Hq * 3 * p.D * p.esize);
+    return qv + (size_t)p.B * p.Hq * kDecodeMaxSplits * (p.D + 2) * sizeof(float);
+}
+
+size_t est_rows_bytes(const Problem &p) {
+    return ((size_t)p.Hq * kEstRows * kEstMaxSplits * 2 + (size_t)p.Hq * kEstRows * 2) * sizeof(float);
+}
+
+size_t est_scratch_bytes(const Problem &p) {
+    return est_rows_bytes(p) + (size_t)p.Hq * 2 * (256 + 4 + kTopkParts * 2) * 4;
+}
+
 static bool misaligned(const void *ptr, uintptr_t a) { return ptr != nullptr && ((uintptr_t)ptr & (a - 1)) != 0; }
 
 Layout layout_for(const Problem &p) {

@@ -114,6 +114,8 @@ int launch_attention(const Problem &p, void *out, float *lse, const void *ws, co
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,
                   double rope_base, float k_scale, void *ws, const Layout &L, void *stream,
                   void *scratch_base = nullptr);
+// splits of the decode's key range per KV group (its partials are sized for this many)
+constexpr int kDecodeMaxSplits = 256;
 size_t decode_scratch_bytes(const Problem &p);
 // the static device array that holds the decode scratch for dca_decode_static:
 // its size, and its address on the current device (looked up once per device)
@@ -121,6 +123,14 @@ constexpr size_t kDecodeStaticScratchBytes = DCA_DECODE_STATIC_SCRATCH_BYTES;
 int decode_static_scratch(void **ptr);
 // online vertical-slash estimation over the keys rotated at their own index
 // (the pre-pass run with C >= S, W = 0, keys only)
+// query rows it scores (the last n <= 64), the splits of the row statistics
+// per row, and the workgroups of the selection per (head, list)
+constexpr int kEstRows = 64;
+constexpr int kEstMaxSplits = 256;
+constexpr int kTopkParts = 16;
+// scratch bytes: the row statistics and combined rows, then the selection's
+// histograms, state and counts (host arithmetic in api.cpp)
+size_t est_rows_bytes(const Problem &p);
 size_t est_scratch_bytes(const Problem &p);
 int launch_vs_estimate(const Problem &p, int n_last, int n_vertical, int n_slash, int n_forced, const void *q,
                        const void *ws, const Layout &L, size_t scratch, float *vscore, float *sscore,

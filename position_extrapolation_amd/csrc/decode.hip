@@ -32,7 +32,7 @@
 
 namespace dca {
 
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = kDecodeMaxSplits;
 
 struct DecodeArgs {
     const void *q, *k, *v;       // new token: q [B][Hq][D], k and v [B][Hkv][D]
@@ -320,11 +320,6 @@ static int launch_decode_t(const Problem &p, const void *q, const void *k, const
     if (err) return err;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)(p.B * p.Hq)), dim3(kCombineThreads), 0, s, a);
     return (int)hipGetLastError();
-}
-
-size_t decode_scratch_bytes(const Problem &p) {
-    const size_t qv = ((size_t)p.B * p.Hq * 3 * p.D * p.esize + 255) & ~(size_t)255;
-    return qv + (size_t)p.B * p.Hq * kMaxSplits * (p.D + 2) * sizeof(float);
 }
 
 int launch_decode(const Problem &p, const void *q, const void *k, const void *v, void *out, float *lse,

@@ -39,8 +39,6 @@
 
 namespace dca {
 
-constexpr int kEstRows = 64;          // query rows scored: the last n <= 64
-constexpr int kEstMaxSplits = 256;
 constexpr int64_t kEstRowstatWaves = 8192;   // targets for the two score passes
 constexpr int64_t kEstSumsWaves = 4096;
 
@@ -307,7 +305,6 @@ __global__ __launch_bounds__(64) void est_sums_kernel(EstArgs a) {
 //   est_topk_write   per range: its picks in index order, at the offset the
 //                    earlier ranges' counts give; ties go to the smaller index
 // ---------------------------------------------------------------------------
-constexpr int kTopkParts = 16;          // workgroups per (head, list)
 constexpr int kTopkBlock = 256;         // threads per workgroup
 constexpr int kTopkPer = 8;             // elements per thread and step
 constexpr int kTopkStep = kTopkBlock * kTopkPer;
@@ -596,14 +593,6 @@ static int launch_est_t(const Problem &p, int n_last, const void *q, const void 
         hipLaunchKernelGGL((est_sums_kernel<T, D>), dim3((unsigned)(set_rows * p.G)), dim3(64), 0, s, as);
     }
     return (int)hipGetLastError();
-}
-
-// row statistics and combined rows, then the selection's histograms, state and counts
-static size_t est_rows_bytes(const Problem &p) {
-    return ((size_t)p.Hq * kEstRows * kEstMaxSplits * 2 + (size_t)p.Hq * kEstRows * 2) * sizeof(float);
-}
-size_t est_scratch_bytes(const Problem &p) {
-    return est_rows_bytes(p) + (size_t)p.Hq * 2 * (256 + 4 + kTopkParts * 2) * 4;
 }
 
 int launch_vs_estimate(const Problem &p, int n_last, int n_vertical, int n_slash, int n_forced, const void *q,
