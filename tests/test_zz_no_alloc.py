@@ -118,3 +118,54 @@ def test_decode_static_rejects_scratch_past_the_array():
         api.dca_decode_static(q, kv, kv.clone(), out, None, 10, S, C, W, 1e7, 1.0, shape, ws, nbytes)
     assert e.value.status == api.DCA_E_UNSUPPORTED
     assert "static array" in str(e.value)
+
+
+def _decode_case(Hq, Hkv, D, S, C, W, prompt, seed):
+    w = workloads.Workload("t", 1, Hq, Hkv, D, S, C, W, "bf16", 0.5, True)
+    q, k, v = synth.make_qkv(w, seed=seed, device=DEV)
+    shape = api.shape_of(q, k)
+    nbytes = api.dca_chunk_workspace_size(S, prompt, C, W, shape)
+    ws = api.alloc_workspace(nbytes, DEV)
+    o = torch.empty_like(q[:, :, :prompt])
+    api.dca_prefill_chunk(q[:, :, :prompt].contiguous(), k[:, :, :prompt].contiguous(),
+                          v[:, :, :prompt].contiguous(), o, None, 0, prompt, S, C, W, w.rope_base, w.yarn_scale,
+                          None, shape, ws, nbytes)
+    tok = tuple(t[:, :, prompt].contiguous() for t in (q, k, v))
+    out = torch.empty_like(tok[0])
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+
+    def call():
+        api.dca_decode_static(*tok, out, lse, prompt, S, C, W, w.rope_base, w.yarn_scale, shape, ws, nbytes)
+
+    return call, out, lse
+
+
+def test_decode_static_in_a_graph():
+    say("[decode static graph] 40/8 heads, d = 128, pos 8000; between replays an eager 8/2-head, d = 64 call")
+    call, out, lse = _decode_case(40, 8, 128, 9000, 2048, 256, 8000, seed=90)
+    other, oo, ol = _decode_case(8, 2, 64, 3000, 1024, 128, 2500, seed=91)
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    other()
+    torch.cuda.synchronize()
+    ref_oo = oo.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        other()                                  # overwrites the shared scratch
+        torch.cuda.synchronize()
+        assert torch.equal(oo, ref_oo)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {r}"
+    say("  three replays identical to the eager call")
