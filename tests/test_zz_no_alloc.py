@@ -3,7 +3,9 @@ scratch lives in the library's static device array), against dca_decode
 through the C ABI: bit-identical outputs on two calls in a row, the second
 with a smaller problem, so that whatever the first call left in the shared
 array cannot leak into the second. Also: a problem whose scratch exceeds the
-array is rejected before any launch."""
+array is rejected before any launch, and the call captured in a HIP graph
+replays bit for bit while a smaller eager call overwrites the array between
+replays."""
 
 from __future__ import annotations
 
