@@ -237,9 +237,11 @@ int dca_decode(const void *q, const void *k, const void *v, void *out, float *ls
  * workspace then only needs the key/value cache: any workspace for this
  * sequence from dca_fused_workspace_size, dca_workspace_size or
  * dca_chunk_workspace_size (mask NULL). A call whose scratch exceeds the
- * array returns DCA_E_UNSUPPORTED and enqueues nothing. The first call on a
- * device looks up the array's address there (a HIP call, no allocation); no
- * call allocates or frees memory. Every call on one GPU shares that GPU's
+ * array returns DCA_E_UNSUPPORTED and enqueues nothing. The stream's device
+ * must be the current device (the array's copy on that device is the one
+ * the kernels use); otherwise DCA_E_INVALID, nothing enqueued. The first
+ * call on a device looks up the array's address there (a HIP call, no
+ * allocation); no call allocates or frees memory. Every call on one GPU shares that GPU's
  * array, whose contents the last call left (nothing in it needs to start at
  * zero): calls that overlap in time on one GPU -- on different streams or
  * host threads -- race on it and must not be made. */

@@ -528,7 +528,10 @@ static int decode_call(const void *q, const void *k, const void *v, void *out, f
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
     void *scratch_base = nullptr;
     if (static_scratch) {
-        const int err = decode_static_scratch(&scratch_base);
+        const int err = decode_static_scratch(stream, &scratch_base);
+        if (err == kStaticScratchWrongDevice)
+            return fail(DCA_E_INVALID, "the stream belongs to another device than the current one; make the "
+                                       "stream's device current before the call");
         if (err) return device_fail(err, "static scratch lookup");
     }
     const float k_scale = yarn_scale * p.softmax_scale * 1.4426950408889634f;

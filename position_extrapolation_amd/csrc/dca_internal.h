@@ -118,9 +118,12 @@ int launch_decode(const Problem &p, const void *q, const void *k, const void *v,
 constexpr int kDecodeMaxSplits = 256;
 size_t decode_scratch_bytes(const Problem &p);
 // the static device array that holds the decode scratch for dca_decode_static:
-// its size, and its address on the current device (looked up once per device)
+// its size, and its address on the current device (looked up once per
+// device); kStaticScratchWrongDevice when a non-null stream belongs to
+// another device than the current one
 constexpr size_t kDecodeStaticScratchBytes = DCA_DECODE_STATIC_SCRATCH_BYTES;
-int decode_static_scratch(void **ptr);
+constexpr int kStaticScratchWrongDevice = -1;
+int decode_static_scratch(void *stream, void **ptr);
 // online vertical-slash estimation over the keys rotated at their own index
 // (the pre-pass run with C >= S, W = 0, keys only)
 // query rows it scores (the last n <= 64), the splits of the row statistics

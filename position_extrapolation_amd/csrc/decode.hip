@@ -348,11 +348,19 @@ constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static void *g_scratch_ptr[kMaxDevices];
 
-int decode_static_scratch(void **ptr) {
+int decode_static_scratch(void *stream, void **ptr) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return (int)e;
     if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    if (stream != nullptr) {
+        // the kernels run on the stream's device: its copy of the array is
+        // the one they may touch, and it is looked up with that device current
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return (int)e;
+        if (sdev != dev) return kStaticScratchWrongDevice;
+    }
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (g_scratch_ptr[dev] == nullptr) {
         // once per device, with that device current

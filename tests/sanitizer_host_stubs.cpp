@@ -24,7 +24,7 @@ int launch_decode(const Problem &, const void *, const void *, const void *, voi
                   const Layout &, void *, void *) {
     return no_device();
 }
-int decode_static_scratch(void **) { return no_device(); }
+int decode_static_scratch(void *, void **) { return no_device(); }
 int launch_vs_estimate(const Problem &, int, int, int, int, const void *, const void *, const Layout &, size_t,
                        float *, float *, int32_t *, int32_t *, void *) {
     return no_device();
