@@ -893,9 +893,11 @@ def test_chunk_reads_only_earlier_blocks():
 # decode: one new token at index pos against the cache a prefill left behind
 # ---------------------------------------------------------------------------
 
-def _decode_run(q, k, v, w, prompt, steps):
+def _decode_run(q, k, v, w, prompt, steps, yarn=None):
     """Prefill rows [0, prompt) as one block (when prompt > 0), then decode the
-    tokens prompt .. prompt + steps - 1 one at a time on the same workspace."""
+    tokens prompt .. prompt + steps - 1 one at a time on the same workspace
+    (YaRN temperature: the workload's, unless given)."""
+    yarn = w.yarn_scale if yarn is None else yarn
     shape = api.shape_of(q, k)
     S = w.seq
     nbytes = api.dca_chunk_workspace_size(S, max(prompt, 1), w.chunk, w.window, shape)
@@ -904,13 +906,13 @@ def _decode_run(q, k, v, w, prompt, steps):
         o = torch.empty_like(q[:, :, :prompt])
         api.dca_prefill_chunk(q[:, :, :prompt].contiguous(), k[:, :, :prompt].contiguous(),
                               v[:, :, :prompt].contiguous(), o, None, 0, prompt, S, w.chunk, w.window, w.rope_base,
-                              w.yarn_scale, None, shape, ws, nbytes)
+                              yarn, None, shape, ws, nbytes)
     outs, lses = [], []
     for pos in range(prompt, prompt + steps):
         o = torch.empty_like(q[:, :, pos])
         l = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
         api.dca_decode(q[:, :, pos].contiguous(), k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), o, l, pos, S,
-                       w.chunk, w.window, w.rope_base, w.yarn_scale, shape, ws, nbytes)
+                       w.chunk, w.window, w.rope_base, yarn, shape, ws, nbytes)
         outs.append(o)
         lses.append(l)
     torch.cuda.synchronize()
@@ -1364,3 +1366,83 @@ def test_vs_estimate_finds_planted_pattern_and_drives_sparse_prefill():
     rows = np.array([S - 1, S - 30, 12000, 700])
     ref, _ = _oracle(q, k, v, rows, w, vertical=vert.cpu().long(), slash=slash.cpu().long())
     assert _err(out[:, :, torch.as_tensor(rows, device=DEV)], ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# seeded random configurations: every entry point over the supported domain
+# ---------------------------------------------------------------------------
+
+_N_RANDOM = 40
+
+
+def _random_case(i):
+    """One seeded draw over the supported domain: dtype, head_dim, batch, GQA
+    ratio, chunk C (a multiple of 64), window W (0, C or between), sequence
+    length (from a single row to a few thousand, ragged), YaRN temperature,
+    entry point (whole-sequence, fused rotation, chunked with a random block,
+    decode) and, for the prefill entry points, sometimes a vertical-slash
+    mask with small random budgets."""
+    rng = np.random.default_rng(7000 + i)
+    c = {}
+    c["dtype"] = "bf16" if rng.random() < 0.7 else "f32"
+    c["D"] = int(rng.choice([64, 128]))
+    c["B"] = 1 if rng.random() < 0.75 else 2
+    c["Hkv"] = int(rng.choice([1, 2]))
+    c["G"] = int(rng.choice([1, 2, 3, 5, 8]))
+    c["C"] = 64 * int(rng.integers(1, 10))
+    c["S"] = int(rng.integers(1, 65)) if rng.random() < 0.15 else int(rng.integers(65, 2600))
+    c["W"] = int(rng.choice([0, c["C"], int(rng.integers(0, c["C"] + 1))]))
+    c["yarn"] = float(rng.choice([1.0, 1.1386294361]))
+    c["mode"] = str(rng.choice(["prefill", "fused", "chunked", "decode"]))
+    c["block"] = 64 * int(rng.integers(1, 9))
+    c["steps"] = min(c["S"], int(rng.integers(1, 9)))
+    c["mask"] = c["mode"] != "decode" and rng.random() < 0.35
+    c["nv"] = int(rng.integers(1, min(c["S"], 48) + 1))
+    c["ns"] = int(rng.integers(1, min(c["S"], 48) + 1))
+    c["forced"] = int(rng.integers(1, min(c["nv"], c["ns"], 8) + 1))
+    return c
+
+
+@pytest.mark.parametrize("i", range(_N_RANDOM))
+def test_random_configuration(i):
+    c = _random_case(i)
+    say(f"[random {i}] {c}")
+    dtype, S, C, W = c["dtype"], c["S"], c["C"], c["W"]
+    Hq = c["Hkv"] * c["G"]
+    w = workloads.Workload("t", c["B"], Hq, c["Hkv"], c["D"], S, C, W, dtype, 0.5 if dtype == "bf16" else 1.0,
+                           False)
+    q, k, v = synth.make_qkv(w, seed=7000 + i, device=DEV)
+    yarn = c["yarn"]
+    vert = slash = vd = sd = None
+    if c["mask"]:
+        # a few forced entries (offset 0 keeps every row's diagonal tile), the
+        # rest drawn from the whole sequence
+        vn, sn = synth.vs_mask(Hq, S, c["nv"], c["ns"], seed=7000 + i, forced=c["forced"])
+        vert, slash = torch.from_numpy(vn), torch.from_numpy(sn)
+        vd, sd = vert.to(DEV), slash.to(DEV)
+    if c["mode"] == "decode":
+        prompt = S - c["steps"]
+        out, lse = _decode_run(q, k, v, w, prompt, c["steps"], yarn=yarn)
+        rows = np.arange(prompt, S)
+        got, got_lse = out, lse
+    else:
+        if c["mode"] == "chunked":
+            out, lse = api.prefill_chunked(q, k, v, C, W, c["block"], w.rope_base, yarn, vertical=vd, slash=sd,
+                                           return_lse=True)
+        else:
+            out, lse = api.prefill(q, k, v, C, W, w.rope_base, yarn, vertical=vd, slash=sd, return_lse=True,
+                                   fused=c["mode"] == "fused")
+        torch.cuda.synchronize()
+        rows = np.arange(S) if S <= 700 else synth.sample_rows(S, C, W, 96, seed=i)
+        rows_t = torch.as_tensor(rows, device=DEV)
+        got, got_lse = out[:, :, rows_t], lse[:, :, rows_t]
+    rows_c = torch.as_tensor(rows, dtype=torch.int64)
+    ref, ref_lse = O.dca_prefill_rows(q[:, :, rows_c.to(DEV)].cpu(), rows_c, k.cpu(), v.cpu(), C, W, w.rope_base,
+                                      yarn, vertical=vert, slash=slash)
+    err, lerr = _err(got, ref), _err(got_lse, ref_lse)
+    say(f"  {len(rows)} rows x {c['B'] * Hq} heads: max abs err out={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL[dtype]
+    assert lerr <= (1e-4 if dtype == "f32" else 2e-2)
+    if dtype == "bf16":
+        g = got.double().cpu()
+        assert ((g - ref).abs() <= ref.abs() * 2.0 ** -8 + 2e-3).all()
