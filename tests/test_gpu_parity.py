@@ -595,6 +595,51 @@ def test_vs_needles_1m():
     assert same and far > 0.2
 
 
+@pytest.mark.parametrize("g", [0, 7])
+def test_vs_estimate_1m_group(g):
+    """The online vertical-slash estimate at the 1M shape with the benchmark's
+    budgets (1000 columns, 2000 offsets, the first 64 of each forced, the last
+    64 rows), on the shared seed-0 input: for the five query heads of KV group
+    g, the column and diagonal scores against the oracle's, the lists exactly
+    the selection rule applied to the kernel's own scores, and differing from
+    the oracle's lists only at the budget's edge, within twice the measured
+    score error."""
+    m = _one_m()
+    w = m["w"]
+    S, n_last, nv, ns, forced = w.seq, 64, 1000, 2000, 64
+    say(f"[vs estimate 1M] KV group {g}: S={S} n_last={n_last} nv={nv} ns={ns} forced={forced}")
+    if "estimate" not in m:
+        vert, slash, vs, ss = api.vs_estimate(m["q"], m["k"], nv, ns, forced, n_last, w.rope_base, w.yarn_scale,
+                                              return_scores=True)
+        torch.cuda.synchronize()
+        m["estimate"] = (vert.cpu(), slash.cpu(), vs.cpu(), ss.cpu())
+    vert, slash, vs, ss = m["estimate"]
+    G = w.n_q_heads // w.n_kv_heads
+    hs = range(g * G, (g + 1) * G)
+    rows = torch.arange(S - n_last, S)
+    q_last = m["q"][0, g * G:(g + 1) * G, S - n_last:].cpu()
+    ref_vs, ref_ss = O.vs_scores(q_last, rows, m["kc"][0, g:g + 1], w.rope_base, w.yarn_scale)
+    ev = (vs[g * G:(g + 1) * G].double() - ref_vs).abs().max().item()
+    es = (ss[g * G:(g + 1) * G].double() - ref_ss).abs().max().item()
+    say(f"  score err vertical={ev:.3e} slash={es:.3e} (largest scores {ref_vs.max().item():.3e}, "
+        f"{ref_ss.max().item():.3e})")
+    # on iid inputs every column and diagonal scores about 64 / S, so the
+    # bound is relative to the largest score: 2^-9, one bf16 rounding of the
+    # rotated keys and queries (measured: 4.4e-4 of it)
+    assert ev <= 2e-3 * ref_vs.abs().max().item() and es <= 2e-3 * ref_ss.abs().max().item()
+    for j, h in enumerate(hs):
+        assert vert[h].long().tolist() == O.top_with_forced(vs[h].double(), nv, forced).tolist()
+        assert slash[h].long().tolist() == O.top_with_forced(ss[h].double(), ns, forced).tolist()
+        for got, sc, budget, err in ((vert[h], ref_vs[j], nv, ev), (slash[h], ref_ss[j], ns, es)):
+            a, b = set(got.tolist()), set(O.top_with_forced(sc, budget, forced).tolist())
+            if a == b:
+                continue
+            edge = min(float(sc[i]) for i in b if i >= forced)
+            for i in a ^ b:
+                assert abs(float(sc[i]) - edge) <= 2 * err + 1e-12, (h, i)
+    say(f"  lists of heads {hs.start}..{hs.stop - 1}: the rule on the kernel's scores; oracle's up to edge ties")
+
+
 def test_planted_needles_bf16():
     """For chosen rows, overwrite one key so that its rotated copy is a large
     multiple of the row's rotated query under the pair's region; the output of
