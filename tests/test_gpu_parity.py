@@ -1511,3 +1511,64 @@ def test_random_configuration(i):
     assert lerr <= (1e-4 if dtype == "f32" else 2e-2)
     if dtype == "bf16":
         assert _within_rounding(got, ref, v, rows, c["G"])
+
+
+_N_RANDOM_EST = 32
+
+
+def _random_estimate_case(i):
+    """One seeded draw over the online estimate's domain: dtype, head_dim, GQA
+    ratio, sequence length (inside one key tile, one off a multiple of the
+    8192 scores the selection stages at a time, or up to 12K), the number of
+    scored rows (1 to 64), both budgets (1 to the whole sequence), the forced
+    head (0 to the smaller budget, at most 64) and the YaRN temperature."""
+    rng = np.random.default_rng(9000 + i)
+    c = {"dtype": "bf16" if rng.random() < 0.7 else "f32", "D": int(rng.choice([64, 128])),
+         "Hkv": int(rng.choice([1, 2])), "G": int(rng.choice([1, 2, 3, 5]))}
+    u = rng.random()
+    if u < 0.15:
+        c["S"] = int(rng.integers(1, 65))
+    elif u < 0.35:
+        c["S"] = max(1, 8192 * int(rng.integers(1, 3)) + int(rng.integers(-1, 2)))
+    else:
+        c["S"] = int(rng.integers(65, 12000))
+    S = c["S"]
+    c["n_last"] = int(rng.integers(1, min(64, S) + 1))
+    c["nv"] = S if rng.random() < 0.1 else int(rng.integers(1, min(S, 3000) + 1))
+    c["ns"] = S if rng.random() < 0.1 else int(rng.integers(1, min(S, 3000) + 1))
+    c["forced"] = int(rng.integers(0, min(c["nv"], c["ns"], 64) + 1))
+    c["yarn"] = float(rng.choice([1.0, 1.1386294361]))
+    return c
+
+
+@pytest.mark.parametrize("i", range(_N_RANDOM_EST))
+def test_random_estimate(i):
+    c = _random_estimate_case(i)
+    say(f"[random estimate {i}] {c}")
+    dtype, S, n_last, nv, ns, forced = c["dtype"], c["S"], c["n_last"], c["nv"], c["ns"], c["forced"]
+    Hq = c["Hkv"] * c["G"]
+    w, (q, k, v) = _est_case(dtype, Hq, c["Hkv"], c["D"], S, seed=9000 + i)
+    vert, slash, vs, ss = api.vs_estimate(q, k, nv, ns, forced, n_last, 1e7, c["yarn"], return_scores=True)
+    torch.cuda.synchronize()
+    rows = torch.arange(S - n_last, S)
+    ref_v, ref_s, ref_vs, ref_ss = O.vs_estimate(q[0, :, rows].cpu(), rows, k[0].cpu(), 1e7, nv, ns, forced,
+                                                 c["yarn"])
+    ev = (vs.double().cpu() - ref_vs).abs().max().item()
+    es = (ss.double().cpu() - ref_ss).abs().max().item()
+    # relative to the largest score (a score is about n_last / S on iid
+    # inputs): one bf16 rounding of the rotated queries and keys, or fp32
+    # sums over up to 12K keys
+    rel = 2e-3 if dtype == "bf16" else 1e-4
+    say(f"  score err vertical={ev:.3e} slash={es:.3e} (largest {ref_vs.max().item():.3e}, {ref_ss.max().item():.3e})")
+    assert ev <= rel * ref_vs.abs().max().item() and es <= rel * ref_ss.abs().max().item()
+    vsc, ssc = vs.double().cpu(), ss.double().cpu()
+    for h in range(Hq):
+        assert vert[h].cpu().long().tolist() == O.top_with_forced(vsc[h], nv, forced).tolist()
+        assert slash[h].cpu().long().tolist() == O.top_with_forced(ssc[h], ns, forced).tolist()
+        for got, ref, sc, err in ((vert[h], ref_v[h], ref_vs[h], ev), (slash[h], ref_s[h], ref_ss[h], es)):
+            a, b = set(got.cpu().tolist()), set(ref.tolist())
+            if a == b:
+                continue
+            edge = min(float(sc[j]) for j in b if j >= forced)
+            for j in a ^ b:
+                assert abs(float(sc[j]) - edge) <= 2 * err + 1e-12, (h, j)
