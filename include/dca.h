@@ -124,7 +124,9 @@ int dca_workspace_size(int64_t seq, int64_t C, int64_t W, const dca_shape *shape
  * attention kernel. q, k, v: device, read-only. out: device, written for
  * every (b, h, i < seq, d). lse: device float32 or NULL (skip). workspace:
  * device, at least dca_workspace_size bytes, 256-byte aligned. out and lse
- * must not overlap q, k, v or the workspace (DCA_E_INVALID). */
+ * must not overlap q, k, v, the workspace or each other; q, k and v must not
+ * overlap the workspace; the mask lists must not overlap the workspace, out
+ * or lse (each DCA_E_INVALID). */
 int dca_prefill(const void *q, const void *k, const void *v, void *out, float *lse,
                 int64_t seq, int64_t C, int64_t W, double rope_base, float yarn_scale,
                 const dca_vs_mask *mask, const dca_shape *shape,
@@ -195,7 +197,9 @@ int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, fl
  * [n_q_heads][seq] or NULL (then kept in the workspace). 1 <= n_vertical,
  * n_slash <= seq and 0 <= n_forced <= both (DCA_E_INVALID). workspace: at
  * least dca_vs_estimate_workspace_size bytes, 256-byte aligned; it holds the
- * keys rotated at their own index and the reduction scratch. */
+ * keys rotated at their own index and the reduction scratch. The four outputs
+ * must not overlap each other, the workspace, q or k, and q and k must not
+ * overlap the workspace (DCA_E_INVALID). */
 int dca_vs_estimate_workspace_size(int64_t seq, const dca_shape *shape, size_t *bytes);
 int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, double rope_base,
                     float yarn_scale, int32_t n_vertical, int32_t n_slash, int32_t n_forced,

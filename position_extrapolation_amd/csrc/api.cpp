@@ -185,6 +185,24 @@ static int check_inputs_vs_workspace(const Problem &p, const void *const *inputs
     return DCA_OK;
 }
 
+// The mask lists are read by the index pass, which writes the workspace; in
+// a chunked prefill they are read again after earlier blocks wrote out and
+// lse. Lists that share memory with the workspace or the outputs would be
+// overwritten before (or while) they are read.
+static int check_mask_overlaps(const Problem &p, const dca_vs_mask *mask, const void *ws, size_t ws_bytes,
+                               const void *out, const float *lse) {
+    if (!p.sparse) return DCA_OK;
+    const size_t vb = (size_t)p.Hq * mask->n_vertical * 4, sb = (size_t)p.Hq * mask->n_slash * 4;
+    const size_t obytes = out ? (size_t)p.B * p.Hq * p.NQ * p.D * p.esize : 0;
+    const size_t lbytes = lse ? (size_t)p.B * p.Hq * p.NQ * 4 : 0;
+    if (overlaps(mask->vertical, vb, ws, ws_bytes) || overlaps(mask->slash, sb, ws, ws_bytes))
+        return fail(DCA_E_INVALID, "a mask list overlaps the workspace");
+    if (overlaps(mask->vertical, vb, out, obytes) || overlaps(mask->slash, sb, out, obytes) ||
+        overlaps(mask->vertical, vb, lse, lbytes) || overlaps(mask->slash, sb, lse, lbytes))
+        return fail(DCA_E_INVALID, "a mask list overlaps out or lse");
+    return DCA_OK;
+}
+
 }  // namespace dca
 
 using namespace dca;
@@ -273,6 +291,7 @@ int dca_vs_index(int64_t seq, int64_t C, int64_t W, const dca_vs_mask *mask, con
     int st = make_problem(seq, C, W, shape, mask, &p);
     if (st) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
+    if ((st = check_mask_overlaps(p, mask, workspace, workspace_bytes, nullptr, nullptr))) return st;
     const int err = launch_vs_index(p, *mask, workspace, L, stream);
     if (err) return device_fail(err, "vertical-slash index launch");
     return ok();
@@ -325,6 +344,7 @@ int dca_prefill(const void *q, const void *k, const void *v, void *out, float *l
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
     const void *inputs[3] = {q, k, v};
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = check_mask_overlaps(p, mask, workspace, workspace_bytes, out, lse))) return st;
     if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     if (p.sparse) {
         const int err = launch_vs_index(p, *mask, workspace, L, stream);
@@ -365,6 +385,7 @@ int dca_prefill_chunk(const void *q, const void *k, const void *v, void *out, fl
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
     const void *inputs[3] = {q, k, v};
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = check_mask_overlaps(p, mask, workspace, workspace_bytes, out, lse))) return st;
     if ((st = do_remap(p, q, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     if (p.sparse) {
         const int err = launch_vs_index(p, *mask, workspace, L, stream);
@@ -402,6 +423,7 @@ int dca_prefill_fused(const void *q, const void *k, const void *v, void *out, fl
     if ((st = check_workspace(p, workspace, workspace_bytes, &L))) return st;
     const void *inputs[3] = {q, k, v};
     if ((st = check_outputs(p, out, lse, inputs, 3, workspace, workspace_bytes))) return st;
+    if ((st = check_mask_overlaps(p, mask, workspace, workspace_bytes, out, lse))) return st;
     if ((st = do_remap(p, nullptr, k, v, rope_base, yarn_scale, workspace, L, stream))) return st;
     if (p.sparse) {
         const int err = launch_vs_index(p, *mask, workspace, L, stream);
@@ -471,10 +493,20 @@ int dca_vs_estimate(const void *q, const void *k, int64_t seq, int32_t n_last, d
     float *ws_scores = (float *)((char *)workspace + scores);   // [2][Hq][seq], used for absent outputs
     float *vs = vertical_score ? vertical_score : ws_scores;
     float *ss = slash_score ? slash_score : ws_scores + p.Hq * p.S;
+    // the four outputs against each other, the workspace and the inputs (q is
+    // [1][Hq][seq][D], k [1][Hkv][seq][D])
     const size_t vb = (size_t)p.Hq * n_vertical * 4, sb = (size_t)p.Hq * n_slash * 4, cb = (size_t)p.Hq * p.S * 4;
-    if (overlaps(vertical, vb, slash, sb) || overlaps(vertical, vb, workspace, workspace_bytes) ||
-        overlaps(slash, sb, workspace, workspace_bytes) || overlaps(vertical_score, cb, slash_score, cb))
-        return fail(DCA_E_INVALID, "outputs overlap each other or the workspace");
+    const void *outs[4] = {vertical, slash, vertical_score, slash_score};
+    const size_t ob[4] = {vb, sb, cb, cb};
+    const size_t qb = (size_t)p.Hq * p.S * p.D * p.esize, kb = (size_t)p.Hkv * p.S * p.D * p.esize;
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], ob[i], outs[j], ob[j])) return fail(DCA_E_INVALID, "outputs overlap each other");
+        if (overlaps(outs[i], ob[i], workspace, workspace_bytes))
+            return fail(DCA_E_INVALID, "an output overlaps the workspace");
+        if (overlaps(outs[i], ob[i], q, qb) || overlaps(outs[i], ob[i], k, kb))
+            return fail(DCA_E_INVALID, "an output overlaps q or k");
+    }
     // keys rotated at their own index, scaled like the attention's
     int err = launch_rope_table(p, rope_base, workspace, L, stream);
     if (err) return device_fail(err, "rope table launch");

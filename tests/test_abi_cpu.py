@@ -97,6 +97,10 @@ def _call_prefill(**over):
     (dict(shape=api.dca_shape(1, 2, 1, 64, 0, -1.0)), api.DCA_E_INVALID),
     (dict(mask=api.dca_vs_mask(None, None, 5, 0)), api.DCA_E_INVALID),
     (dict(mask=api.dca_vs_mask(None, None, -1, 0)), api.DCA_E_INVALID),
+    (dict(mask=api.dca_vs_mask(0x50000000 + 4096, 0xA1000000, 10, 10)), api.DCA_E_INVALID),  # list in the workspace
+    (dict(mask=api.dca_vs_mask(0xA0000000, 0x40000000 + 64, 10, 10)), api.DCA_E_INVALID),    # list inside out
+    (dict(mask=api.dca_vs_mask(0xA0000000, 0xB0000000, 10, 10), lse=0xB0000000 - 16),
+     api.DCA_E_INVALID),                                                                    # list inside lse
     (dict(seq=1 << 31), api.DCA_E_UNSUPPORTED),
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(over, status):
@@ -140,11 +144,12 @@ def test_fused_workspace_size():
 def _call_chunk(**over):
     sh = api.make_shape(1, 2, 1, 64, torch.float32)
     args = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, lse=None, q_offset=512, n_rows=256,
-                seq=2048, C=512, W=128, base=1e7, yarn=1.0, ws=0x50000000, ws_bytes=1 << 30)
+                seq=2048, C=512, W=128, base=1e7, yarn=1.0, mask=None, ws=0x50000000, ws_bytes=1 << 30)
     args.update(over)
     return api.lib().dca_prefill_chunk(args["q"], args["k"], args["v"], args["out"], args["lse"], args["q_offset"],
                                        args["n_rows"], args["seq"], args["C"], args["W"], args["base"],
-                                       args["yarn"], None, ctypes.byref(sh), args["ws"], args["ws_bytes"], None)
+                                       args["yarn"], None if args["mask"] is None else ctypes.byref(args["mask"]),
+                                       ctypes.byref(sh), args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -156,6 +161,8 @@ def _call_chunk(**over):
     (dict(out=0x10000000 + 4096), api.DCA_E_INVALID),     # out overlaps q
     (dict(k=None), api.DCA_E_INVALID),
     (dict(v=0x50000000 + 256), api.DCA_E_INVALID),        # v inside the workspace
+    (dict(mask=api.dca_vs_mask(0xA0000000, 0x50000000 + 256, 10, 10)), api.DCA_E_INVALID),   # list in the workspace
+    (dict(mask=api.dca_vs_mask(0x40000000 + 512, 0xA1000000, 10, 10)), api.DCA_E_INVALID),   # list inside out
 ])
 def test_chunk_arguments_rejected_before_any_hip_call(over, status):
     assert _call_chunk(**over) == status
@@ -220,10 +227,35 @@ def _call_estimate(**over):
     (dict(ws_bytes=1 << 20), api.DCA_E_WORKSPACE),
     (dict(slash=0x30000000 + 64), api.DCA_E_INVALID),     # lists overlap
     (dict(k=0x50000000 + 4096), api.DCA_E_INVALID),       # k inside the workspace
+    (dict(vs=0x50000000 + 4096), api.DCA_E_INVALID),      # a score output inside the workspace
+    (dict(vs=0xA0000000, ss=0xA0000000 + 64), api.DCA_E_INVALID),   # the score outputs overlap
+    (dict(ss=0x30000000 - 64), api.DCA_E_INVALID),        # a score output runs into the vertical list
+    (dict(ss=0x10000000 + 4096), api.DCA_E_INVALID),      # a score output inside q
+    (dict(vert=0x20000000 + 128), api.DCA_E_INVALID),     # a list inside k
 ])
 def test_estimate_arguments_rejected_before_any_hip_call(over, status):
     assert _call_estimate(**over) == status
     assert api.dca_last_error() != ""
+
+
+def test_valid_masked_and_scored_calls_without_gpu_report_device_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    # the fake workspace spans [0x50000000, 0x90000000): lists and scores above it
+    assert _call_prefill(mask=api.dca_vs_mask(0xA0000000, 0xA1000000, 10, 10)) == api.DCA_E_DEVICE
+    assert _call_chunk(mask=api.dca_vs_mask(0xA0000000, 0xA1000000, 10, 10)) == api.DCA_E_DEVICE
+    assert _call_estimate(vs=0xA0000000, ss=0xA1000000) == api.DCA_E_DEVICE
+
+
+def test_index_and_fused_reject_mask_lists_in_the_workspace():
+    sh = api.make_shape(1, 2, 1, 64, torch.float32)
+    L = api.lib()
+    inside = api.dca_vs_mask(0x50000000 + 4096, 0xA1000000, 10, 10)
+    st = L.dca_vs_index(2048, 512, 128, ctypes.byref(inside), ctypes.byref(sh), 0x50000000, 1 << 30, None)
+    assert st == api.DCA_E_INVALID and "mask list" in api.dca_last_error()
+    st = L.dca_prefill_fused(0x10000000, 0x20000000, 0x30000000, 0x40000000, None, 2048, 512, 128, 1e7, 1.0,
+                             ctypes.byref(inside), ctypes.byref(sh), 0x50000000, 1 << 30, None)
+    assert st == api.DCA_E_INVALID and "mask list" in api.dca_last_error()
 
 
 def test_estimate_workspace_size():
