@@ -444,6 +444,81 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     assert not _pins_pass(mod), f"planted mistake '{name}' not caught"
 
 
+def _mask_and_estimate_pins_pass(mod) -> bool:
+    """A compact set of the mask and estimate pins run against oracle module
+    `mod`: the hand-worked tile fixture, tile activity against pair
+    enumeration (with offsets on tile-distance edges), the estimate's scores
+    against the pairwise brute force, and the selection rule on ties."""
+    try:
+        rows, _, active = _read_fixture("vs_tiles_S512.txt")
+        S = rows["S"][0]
+        vert, slash = torch.tensor(rows["vertical"]), torch.tensor(rows["slash"])
+        vt, dd = mod.vs_tile_lists(vert, slash, S)
+        if vt.tolist() != rows["VT"] or dd.tolist() != rows["D"]:
+            return False
+        for t, want in active.items():
+            kts = torch.arange(t + 1)
+            if kts[mod.vs_tile_active(vert, slash, torch.full_like(kts, t), kts)].tolist() != want:
+                return False
+        # columns and offsets on the edges of tiles and tile distances
+        for vv, ss in (([63, 64], [1]), ([], [64]), ([], [63, 127]), ([128], [0])):
+            vs_, ss_ = set(vv), set(ss)
+            for t in range(4):
+                for kt in range(t + 1):
+                    brute = any((j in vs_) or ((i - j) in ss_)
+                                for i in range(64 * t, 64 * t + 64) for j in range(64 * kt, 64 * kt + 64))
+                    got = bool(mod.vs_tile_active(torch.tensor(vv, dtype=torch.int64), torch.tensor(ss),
+                                                  torch.tensor([t]), torch.tensor([kt]))[0])
+                    if got != brute:
+                        return False
+        Hq, Hkv, S, d, n = 4, 2, 90, 8, 12
+        q = _rand((Hq, n, d), 100)
+        k = _rand((Hkv, S, d), 101)
+        r = torch.arange(S - n, S)
+        vs, ss = mod.vs_scores(q, r, k, 1e4, 1.3)
+        bv, bs = BF.vs_scores(q.numpy(), r.tolist(), k.numpy(), 1e4, 1.3)
+        if not (np.allclose(vs.numpy(), bv, rtol=0, atol=1e-12) and np.allclose(ss.numpy(), bs, rtol=0, atol=1e-12)):
+            return False
+        score = torch.tensor([9.0, 1.0, 5.0, 5.0, 0.5, 5.0, 7.0], dtype=torch.float64)
+        return (mod.top_with_forced(score, 4, 2).tolist() == [0, 1, 2, 6]
+                and mod.top_with_forced(score, 3, 0).tolist() == [0, 2, 6])
+    except Exception:
+        return False
+
+
+MASK_MUTATIONS = {
+    "slash interval starts one low": ("lo = torch.clamp(TILE * dlt - (TILE - 1), min=0)",
+                                      "lo = torch.clamp(TILE * dlt - TILE, min=0)"),
+    "vertical interval ends one high": ("v_hit = _any_in_interval(vertical, TILE * kt, TILE * kt + TILE - 1)",
+                                        "v_hit = _any_in_interval(vertical, TILE * kt, TILE * kt + TILE)"),
+    "estimate sees one key past the row": ("allowed = keys[None, :] <= rows[:, None]   ",
+                                           "allowed = keys[None, :] <= rows[:, None] + 1"),
+    "estimate diagonal index off by one": ("offs = rows[:, None] - keys[None, :]   ",
+                                           "offs = rows[:, None] - keys[None, :] + 1"),
+    "estimate logit scale dropped": ("logits = scale * (q_rot @ k_rot.T)", "logits = (q_rot @ k_rot.T)"),
+    "forced head dropped": ("f = min(forced, budget, n)", "f = 0"),
+    "ties to the larger index": ("order = torch.sort(-score[f:].to(F64), stable=True).indices[:take]",
+                                 "order = (rest.numel() - 1 - torch.sort(-score[f:].to(F64).flip(0), "
+                                 "stable=True).indices)[:take]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MASK_MUTATIONS))
+def test_mask_and_estimate_pins_catch_planted_mistake(name, tmp_path):
+    import importlib.util
+
+    src = open(O.__file__).read()
+    old, new = MASK_MUTATIONS[name]
+    assert src.count(old) == 1, name
+    path = tmp_path / "mutant_oracle.py"
+    path.write_text(src.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location("mutant_oracle", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _mask_and_estimate_pins_pass(O)
+    assert not _mask_and_estimate_pins_pass(mod), f"planted mistake '{name}' not caught"
+
+
 # ---------------------------------------------------------------------------
 # online vertical-slash estimation (continuous positions)
 # ---------------------------------------------------------------------------
